@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of the Lightning Indexer forward pass on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+li_metadata (work list) + li_forward (scores, ReLU / weight / head sum, fused
+top-k, outputs).  Default workload: prefill, B=1, S1=S2=4096, BSND, 64
+query-index heads, D=128, bf16 q/k/w, top-2048, right-down causal mask.
+
+Prints one JSON line with the throughput (query tokens per second), the
+roofline of the dominant kernel (its average duration measured with HIP events
+on the launch stream, algorithmic FLOP = 2 * N1 * D per visible query-key pair)
+and the CPU oracle timed on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload prefill|decode|varlen|longfp8|tiny]
+                  [--no-cpu-baseline] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from score_top_token_amd import binding, synth  # noqa: E402
+
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp8": 5033.2}   # dense MFMA, MI355X
+PEAK_HBM_GBS = 8000.0
+HBM_BOUND = {"decode"}
+
+# measured rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dominant
+# kernel for the default workload, scaled by the plain-copy calibration; None until taken
+TRAFFIC_BYTES = {}
+
+
+def visible_pairs(inst) -> int:
+    tot = 0
+    for s1, s2 in zip(inst["seqlens_q"], inst["seqlens_k"]):
+        if inst["mask_mode"] == 0:
+            tot += s1 * s2
+        else:
+            i = np.arange(s1, dtype=np.int64)
+            tot += int(np.clip(i + s2 - s1 + 1, 0, s2).sum())
+    return tot
+
+
+def algorithmic_bytes(inst) -> int:
+    """Bytes the path must move at least: q, w, the visible K rows, descales,
+    block-table entries used, and the outputs (indices + values)."""
+    esz = 1 if inst["qk_dtype"] == "fp8" else 2
+    rows = sum(inst["seqlens_q"])
+    q = rows * inst["n1"] * 128 * esz
+    w = rows * inst["n1"] * (4 if inst["w_dtype"] == "fp32" else 2)
+    keys = sum(min(s2, s2 if inst["mask_mode"] == 0 else s2) for s2 in inst["seqlens_k"])
+    k = keys * 128 * esz
+    extra = 0
+    if inst["qk_dtype"] == "fp8":
+        extra += rows * 4 + keys * 4
+    if inst["layout_k"] == "PA_BSND":
+        bs = inst["block_size"]
+        extra += sum(-(-s2 // bs) for s2 in inst["seqlens_k"]) * 4
+    out = rows * inst["topk"] * 8
+    return q + w + k + extra + out
+
+
+def to_device(inst, dev):
+    g = {n: (inst[n].to(dev) if isinstance(inst.get(n), torch.Tensor) else None)
+         for n in ("q", "k", "w", "q_descale", "k_descale", "cu_seqlens_q", "cu_seqlens_k",
+                   "seqused_k", "block_table")}
+    if inst["layout_k"] == "PA_BSND":
+        kc = inst["k"]
+        base = kc.as_strided((kc.shape[0], kc.stride(0)), (kc.stride(0), 1)).to(dev)
+        g["k"] = base.as_strided(kc.shape, kc.stride())
+    return g
+
+
+def cpu_baseline(inst, max_rows: int, cores: int):
+    import oracle
+    ob = oracle.Bound(inst)
+    total = ob.num_rows
+    nrows = min(total, max_rows)
+    rows = np.unique(np.linspace(0, total - 1, nrows).round().astype(np.int64))
+    t0 = time.perf_counter()
+    ob.forward(rows=rows, nthreads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(rows)} of {total} query rows, evenly spaced (every "
+                      f"{total // max(1, len(rows))}th row), plain fp64 C oracle with {cores} "
+                      f"POSIX threads; {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill", choices=sorted(synth.PRESETS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+              "the multi-GPU sharding is a design note, not an implemented path", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    binding.load()
+    inst = synth.make(args.workload, args.seed)
+    g = to_device(inst, dev)
+    p = binding.problem_for(inst, g["k"])
+    st, meta_bytes = binding.li_metadata_size(p)
+    assert st == 0, binding.li_status_str(st)
+    st, ws_bytes = binding.li_workspace_size(p)
+    assert st == 0, binding.li_status_str(st)
+    meta = torch.empty(max(meta_bytes, 16), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    rows = sum(inst["seqlens_q"])
+    topk = inst["topk"]
+    idx = torch.empty(rows * topk, dtype=torch.int32, device=dev)
+    val = torch.empty(rows * topk, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    ptr = lambda t: None if t is None else t.data_ptr()
+
+    def metadata():
+        st = binding.li_metadata(p, ptr(g["cu_seqlens_q"]), ptr(g["cu_seqlens_k"]),
+                                 ptr(g["seqused_k"]), meta.data_ptr(), meta.numel(), sh)
+        assert st == 0, binding.li_status_str(st)
+
+    def forward():
+        st = binding.li_forward(p, ptr(g["q"]), ptr(g["k"]), ptr(g["w"]), ptr(g["q_descale"]),
+                                ptr(g["k_descale"]), ptr(g["cu_seqlens_q"]),
+                                ptr(g["cu_seqlens_k"]), ptr(g["seqused_k"]),
+                                ptr(g["block_table"]), meta.data_ptr(), ws.data_ptr(),
+                                ws.numel(), idx.data_ptr(), val.data_ptr(), sh)
+        assert st == 0, binding.li_status_str(st)
+
+    # decode streams K from HBM: evict it from the 256 MB infinity cache between steps
+    flush = None
+    if args.workload in HBM_BOUND:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    for _ in range(args.warmup):
+        metadata()
+        forward()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        if flush is not None:
+            flush.fill_(s & 255)
+        metadata()
+        starts[s].record(stream)
+        forward()
+        ends[s].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    fwd_avg = float(np.mean(fwd_ms))
+
+    # the metadata kernel alone (reported separately)
+    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m0.record(stream)
+    for _ in range(10):
+        metadata()
+    m1.record(stream)
+    torch.cuda.synchronize()
+    meta_ms = m0.elapsed_time(m1) / 10
+
+    dtype = inst["qk_dtype"]
+    pairs = visible_pairs(inst)
+    flop = 2.0 * inst["n1"] * 128 * pairs
+    hbm = algorithmic_bytes(inst)
+    ms_step = wall * 1000.0 / args.steps if flush is None else fwd_avg + meta_ms
+    value = rows / (ms_step / 1000.0)
+    if args.workload in HBM_BOUND:
+        achieved = hbm / (fwd_avg / 1000.0) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": TRAFFIC_BYTES.get(args.workload)}
+    else:
+        achieved = flop / (fwd_avg / 1000.0) / 1e12
+        peak = PEAK_TFLOPS[dtype]
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": TRAFFIC_BYTES.get(args.workload)}
+
+    cfg = {"workload": args.workload, "batch": inst["batch"], "seq_len_q": inst["max_seqlen_q"],
+           "seq_len_k": inst["max_seqlen_k"], "query_rows": rows, "heads_q": inst["n1"],
+           "head_dim": 128, "topk": topk, "layout_q": inst["layout_q"],
+           "layout_k": inst["layout_k"], "mask_mode": inst["mask_mode"], "seed": args.seed}
+    out = {
+        "metric": "query-tokens/s (prefill score + top-k), TFLOPS and % of MFMA peak",
+        "value": value, "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": cfg,
+        "forward_ms": fwd_avg, "forward_ms_p10": float(np.percentile(fwd_ms, 10)),
+        "forward_ms_p90": float(np.percentile(fwd_ms, 90)), "metadata_ms": meta_ms,
+        "tflops": flop / (fwd_avg / 1000.0) / 1e12, "algorithmic_flop": flop,
+        "algorithmic_bytes": hbm, "visible_pairs": pairs,
+        "roofline": roof,
+    }
+    if args.workload in HBM_BOUND:
+        out["metric"] = "query-tokens/s (paged decode score + top-k) and % of HBM bandwidth"
+    if not args.no_cpu_baseline:
+        try:
+            cores = min(16, len(os.sched_getaffinity(0)))
+        except AttributeError:
+            cores = min(16, os.cpu_count() or 1)
+        out["cpu_baseline"] = cpu_baseline(inst, args.cpu_rows, cores)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * li.h -- C ABI of the MI355X (gfx950) Lightning Indexer forward pass.
+ *
+ * What it computes.  For every query token t and every key s visible to it
+ *
+ *     I[t,s] = sum_h  w[t,h] * ReLU( q[t,h,:] . k[s,:] )          (D = 128)
+ *
+ * (npu_lightning_indexer_pto page, formula under "功能说明"; the lightning_indexer
+ * CANN API page, "Function", steps 1-3; aclnnLightningIndexerV2 page, "计算公式"),
+ * then, per token, the top-k visible keys: their positions go to sparse_indices and
+ * their scores to sparse_values.  Slots past the number of visible keys hold -1 and
+ * -inf (lightning_indexer page, Constraints).
+ *
+ * The work is split in two calls, like the pages' lightning_indexer_metadata +
+ * lightning_indexer pair (lightning_indexer page, "Prototype": the metadata call
+ * does the load balancing and must precede the indexer), and sizes are queried
+ * first, like the two-phase aclnn interface (aclnnLightningIndexerV2 page: query
+ * the workspace size, then execute).
+ *
+ * Conventions shared by every entry point:
+ *  - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *    allocates no memory, never synchronises the host inside li_metadata or
+ *    li_forward, and keeps no global mutable state: calls are thread-safe and
+ *    may be captured in a HIP graph.  Work is enqueued on `stream` (0 = the null
+ *    stream) and completes asynchronously.
+ *  - Errors are reported only through li_status.  Every argument check that
+ *    needs no device data runs before the first HIP call, so an invalid call
+ *    enqueues nothing.  A problem with zero query rows returns LI_OK and
+ *    launches nothing.
+ *  - Data-dependent preconditions are not checked (undefined behaviour when
+ *    violated): cu_seqlens non-decreasing with cu[B-1] equal to total_q /
+ *    total_k; per-batch lengths <= max_seqlen_q / max_seqlen_k; seqused_k[b] <=
+ *    max_blocks_per_seq * block_size; block_table entries in [0, num_blocks)
+ *    for every block that holds a used key; descales finite and >= 0.
+ *
+ * Semantics fixed where the pages leave them open:
+ *  - Indices are 0-based sequence-local LOGICAL key positions (not offsets into a
+ *    packed TND tensor and not physical paged slots).
+ *  - mask_mode 0: every key of the batch is visible.  mask_mode 3 (rightDownCausal,
+ *    the lower triangle anchored at the bottom-right corner): local query row i of
+ *    a batch with S1_b queries and S2_b keys sees keys s <= i + S2_b - S1_b.
+ *  - Exactly n = min(topk, |visible|) valid entries, stored as the prefix
+ *    [0, n) of each output row; among equal scores the smaller key index wins.
+ *    The order inside the prefix is ascending key index.
+ *  - No 1/sqrt(D) scale is applied.  fp8 inputs are e4m3fn codes whose real value is
+ *    code * descale, with one fp32 descale per query token and per key slot.
+ */
+#ifndef LI_H
+#define LI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LI_OK = 0,
+  LI_ERR_INVALID_ARGUMENT = 1,   /* a value outside the documented range, a missing pointer */
+  LI_ERR_UNSUPPORTED = 2,        /* valid for the pages but not built here (topk > 2048, cmp_ratio > 1) */
+  LI_ERR_WORKSPACE_TOO_SMALL = 3,/* metadata or workspace buffer smaller than the size query said */
+  LI_ERR_HIP = 4                 /* a HIP runtime call failed (launch error) */
+} li_status;
+
+typedef enum {
+  LI_LAYOUT_BSND = 0,            /* [B, S, N, D], batch-padded */
+  LI_LAYOUT_TND = 1,             /* [T, N, D], packed, with inclusive cu_seqlens */
+  LI_LAYOUT_PA_BSND = 2          /* keys only: paged pool [num_blocks, block_size, 1, D] */
+} li_layout;
+
+typedef enum {
+  LI_DT_BF16 = 0,
+  LI_DT_FP8_E4M3 = 1,            /* OCP e4m3fn codes, needs q_descale and k_descale */
+  LI_DT_FP32 = 2,                /* weights only */
+  LI_DT_FP16 = 3
+} li_dtype;
+
+/*
+ * Problem description (host memory, read during the call only).
+ * Ranges follow the pages' constraints (lightning_indexer page, Constraints;
+ * aclnnLightningIndexerV2 page, 约束说明): N of q in [1, 64], N of k = 1, head dim
+ * 128, q and k of one dtype, topk in [1, 2048] (3072..8192 are accepted by the pages
+ * on some hardware and give LI_ERR_UNSUPPORTED here), paged block size in [1, 1024]
+ * with 32-byte-aligned blocks, and axis 0 of the paged pool may be non-contiguous.
+ */
+typedef struct {
+  int32_t batch;                 /* B >= 0                                                  */
+  int32_t max_seqlen_q;          /* BSND: S1.  TND: an upper bound of every S1_b            */
+  int32_t max_seqlen_k;          /* BSND: S2.  TND / PA: an upper bound of every S2_b       */
+  int32_t total_q;               /* TND q: T1 (= cu_seqlens_q[B-1]); else ignored           */
+  int32_t total_k;               /* TND k: T2 (= cu_seqlens_k[B-1]); else ignored           */
+  int32_t num_heads_q;           /* N1 in [1, 64]                                           */
+  int32_t num_heads_k;           /* N2, must be 1                                           */
+  int32_t head_dim;              /* D, must be 128                                          */
+  int32_t topk;                  /* [1, 2048]                                               */
+  int32_t layout_q;              /* li_layout: BSND or TND                                  */
+  int32_t layout_k;              /* li_layout: BSND, TND or PA_BSND                         */
+  int32_t mask_mode;             /* 0 or 3                                                  */
+  int32_t qk_dtype;              /* li_dtype: BF16, FP16 or FP8_E4M3 (q and k alike)        */
+  int32_t w_dtype;               /* li_dtype: BF16 or FP32                                  */
+  int32_t block_size;            /* PA only: [1, 1024], block_size*D*elem % 32 == 0         */
+  int32_t num_blocks;            /* PA only: blocks in the pool (> 0)                       */
+  int32_t max_blocks_per_seq;    /* PA only: columns of block_table (> 0)                   */
+  int32_t cmp_ratio;             /* key compression ratio; only 1 is built                  */
+  int64_t k_block_stride;        /* PA only: elements between pool blocks, >= block_size*D;
+                                    0 means block_size*D (a contiguous pool)                */
+} li_problem;
+
+/* Bytes of the metadata buffer that li_metadata fills for this problem.  Host
+ * only: validates the scalars, makes no HIP call. */
+li_status li_metadata_size(const li_problem* p, size_t* bytes);
+
+/* Bytes of scratch device memory li_forward needs (0 is possible).  Host only. */
+li_status li_workspace_size(const li_problem* p, size_t* bytes);
+
+/*
+ * Builds the work list for li_forward on `stream` (one small kernel).
+ *  cu_seqlens_q : int32 [B], inclusive prefix sums of query lengths; required iff
+ *                 layout_q == TND, must be NULL otherwise.
+ *  cu_seqlens_k : int32 [B], inclusive prefix sums of key lengths; required iff
+ *                 layout_k == TND, must be NULL otherwise.
+ *  seqused_k    : int32 [B], keys used per batch; required iff layout_k == PA_BSND,
+ *                 must be NULL otherwise.
+ *  metadata     : device buffer of at least li_metadata_size bytes, 256-byte aligned.
+ * The metadata stays valid for any li_forward call with the same problem and the
+ * same length arrays; it is read-only for li_forward.
+ */
+li_status li_metadata(const li_problem* p, const int32_t* cu_seqlens_q,
+                      const int32_t* cu_seqlens_k, const int32_t* seqused_k, void* metadata,
+                      size_t metadata_bytes, hipStream_t stream);
+
+/*
+ * Scores every visible (query, key) pair and writes the per-token top-k.
+ *  q            : BSND [B, S1, N1, 128] or TND [T1, N1, 128], contiguous, qk_dtype.
+ *  k            : BSND [B, S2, 1, 128], TND [T2, 1, 128] (contiguous), or the paged
+ *                 pool [num_blocks, block_size, 1, 128] whose block stride is
+ *                 k_block_stride elements (rows inside a block contiguous).
+ *  w            : [B, S1, N1] or [T1, N1], contiguous, w_dtype.
+ *  q_descale    : fp32, one per query token ([B, S1] or [T1]); required iff fp8.
+ *  k_descale    : fp32, one per key slot ([B, S2], [T2], or [num_blocks, block_size]
+ *                 contiguous for the paged pool); required iff fp8.
+ *  cu_seqlens_q, cu_seqlens_k, seqused_k : as for li_metadata (same contents).
+ *  block_table  : int32 [B, max_blocks_per_seq]; required iff layout_k == PA_BSND.
+ *                 Logical key s of batch b lives in row s % block_size of pool
+ *                 block block_table[b][s / block_size].
+ *  metadata     : filled by li_metadata for this problem.
+ *  workspace    : li_workspace_size bytes of device scratch (may be NULL when that
+ *                 size is 0), 256-byte aligned; its contents need no initialisation.
+ *  sparse_indices : int32 [B, S1, 1, topk] or [T1, 1, topk].
+ *  sparse_values  : fp32, same shape, or NULL to skip values (the pages'
+ *                   return_value = 0).
+ * q, k, w and the descales must be 16-byte aligned.
+ */
+li_status li_forward(const li_problem* p, const void* q, const void* k, const void* w,
+                     const float* q_descale, const float* k_descale,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                     const int32_t* seqused_k, const int32_t* block_table,
+                     const void* metadata, void* workspace, size_t workspace_bytes,
+                     int32_t* sparse_indices, float* sparse_values, hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* li_status_str(li_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LI_H */

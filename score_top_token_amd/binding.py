@@ -1,0 +1,236 @@
+"""ctypes binding of the C ABI in include/li.h.
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  The library must have been built (score_top_token_amd.build or
+__graft_entry__.build()); loading fails loudly otherwise -- there is no fallback.
+
+Low level: li_metadata_size, li_workspace_size, li_metadata, li_forward and
+li_status_str take the same arguments as the C functions (device pointers as
+ints, a Problem structure, a raw stream handle).
+
+High level (torch tensors on the GPU, mirroring the lightning_indexer page's
+Prototype section): problem_from(...), lightning_indexer_metadata(...) and
+lightning_indexer(...).  torch only supplies device memory and the stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblightning_indexer.so")
+
+LAYOUT = {"BSND": 0, "TND": 1, "PA_BSND": 2, "PA_BBND": 2}
+DTYPE = {torch.bfloat16: 0, torch.float8_e4m3fn: 1, torch.float32: 2, torch.float16: 3}
+STATUS = {0: "LI_OK", 1: "LI_ERR_INVALID_ARGUMENT", 2: "LI_ERR_UNSUPPORTED",
+          3: "LI_ERR_WORKSPACE_TOO_SMALL", 4: "LI_ERR_HIP"}
+
+EXPORTED = ("li_metadata_size", "li_workspace_size", "li_metadata", "li_forward", "li_status_str")
+
+
+class Problem(ctypes.Structure):
+    """Mirror of li_problem."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("max_seqlen_q", ctypes.c_int32),
+        ("max_seqlen_k", ctypes.c_int32), ("total_q", ctypes.c_int32),
+        ("total_k", ctypes.c_int32), ("num_heads_q", ctypes.c_int32),
+        ("num_heads_k", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("topk", ctypes.c_int32), ("layout_q", ctypes.c_int32), ("layout_k", ctypes.c_int32),
+        ("mask_mode", ctypes.c_int32), ("qk_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32), ("cmp_ratio", ctypes.c_int32),
+        ("k_block_stride", ctypes.c_int64),
+    ]
+
+
+class LIError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+        self.status = status
+
+
+_lib = None
+
+
+def load():
+    """Loads the built HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library missing: {LIB_PATH} (build it first)")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(Problem)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        L.li_metadata_size.argtypes = [P, ctypes.POINTER(sz)]
+        L.li_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
+        L.li_metadata.argtypes = [P, vp, vp, vp, vp, sz, vp]
+        L.li_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.li_status_str.argtypes = [ctypes.c_int]
+        L.li_status_str.restype = ctypes.c_char_p
+        for n in ("li_metadata_size", "li_workspace_size", "li_metadata", "li_forward"):
+            getattr(L, n).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# same-name wrappers of the C entry points
+# ---------------------------------------------------------------------------
+
+def li_metadata_size(p: Problem) -> tuple[int, int]:
+    n = ctypes.c_size_t(0)
+    st = load().li_metadata_size(ctypes.byref(p), ctypes.byref(n))
+    return st, n.value
+
+
+def li_workspace_size(p: Problem) -> tuple[int, int]:
+    n = ctypes.c_size_t(0)
+    st = load().li_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    return st, n.value
+
+
+def li_metadata(p: Problem, cu_seqlens_q, cu_seqlens_k, seqused_k, metadata, metadata_bytes,
+                stream) -> int:
+    return load().li_metadata(ctypes.byref(p), cu_seqlens_q, cu_seqlens_k, seqused_k, metadata,
+                              metadata_bytes, stream)
+
+
+def li_forward(p: Problem, q, k, w, q_descale, k_descale, cu_seqlens_q, cu_seqlens_k, seqused_k,
+               block_table, metadata, workspace, workspace_bytes, sparse_indices, sparse_values,
+               stream) -> int:
+    return load().li_forward(ctypes.byref(p), q, k, w, q_descale, k_descale, cu_seqlens_q,
+                             cu_seqlens_k, seqused_k, block_table, metadata, workspace,
+                             workspace_bytes, sparse_indices, sparse_values, stream)
+
+
+def li_status_str(status: int) -> str:
+    return load().li_status_str(status).decode()
+
+
+# ---------------------------------------------------------------------------
+# torch-facing helpers
+# ---------------------------------------------------------------------------
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise LIError(st, where)
+
+
+def problem_from(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, topk: int, *,
+                 layout_q: str = "BSND", layout_k: str = "BSND", mask_mode: int = 0,
+                 batch_size: Optional[int] = None, max_seqlen_q: Optional[int] = None,
+                 max_seqlen_k: Optional[int] = None, block_table: Optional[torch.Tensor] = None,
+                 cmp_ratio: int = 1) -> Problem:
+    """Fills a Problem from tensor shapes (no device data is read)."""
+    p = Problem()
+    p.num_heads_q = q.shape[-2]
+    p.head_dim = q.shape[-1]
+    p.num_heads_k = k.shape[-2]
+    p.topk = int(topk)
+    p.layout_q, p.layout_k = LAYOUT[layout_q], LAYOUT[layout_k]
+    p.mask_mode = int(mask_mode)
+    p.qk_dtype = DTYPE.get(q.dtype, -1)
+    p.w_dtype = DTYPE.get(w.dtype, -1)
+    p.cmp_ratio = int(cmp_ratio)
+    if layout_q == "TND":
+        p.total_q = q.shape[0]
+        if batch_size is None or max_seqlen_q is None:
+            raise ValueError("TND queries need batch_size and max_seqlen_q")
+        p.batch, p.max_seqlen_q = int(batch_size), int(max_seqlen_q)
+    else:
+        p.batch, p.max_seqlen_q = q.shape[0], q.shape[1]
+    if layout_k == "TND":
+        p.total_k = k.shape[0]
+        if max_seqlen_k is None:
+            raise ValueError("TND keys need max_seqlen_k")
+        p.max_seqlen_k = int(max_seqlen_k)
+    elif layout_k in ("PA_BSND", "PA_BBND"):
+        if block_table is None or max_seqlen_k is None:
+            raise ValueError("paged keys need block_table and max_seqlen_k")
+        p.block_size = k.shape[1]
+        p.num_blocks = k.shape[0]
+        p.max_blocks_per_seq = block_table.shape[1]
+        p.k_block_stride = k.stride(0)
+        p.max_seqlen_k = int(max_seqlen_k)
+    else:
+        p.max_seqlen_k = k.shape[1]
+    return p
+
+
+def lightning_indexer_metadata(p: Problem, *, cu_seqlens_q=None, cu_seqlens_k=None,
+                               seqused_k=None, device=None) -> torch.Tensor:
+    """Allocates and fills the metadata (work list) on the current stream."""
+    st, nbytes = li_metadata_size(p)
+    _check(st, "li_metadata_size")
+    dev = device or (cu_seqlens_q.device if cu_seqlens_q is not None else torch.device("cuda"))
+    meta = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(li_metadata(p, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(seqused_k),
+                       meta.data_ptr(), meta.numel(), stream), "li_metadata")
+    return meta
+
+
+def lightning_indexer(p: Problem, q, k, w, *, metadata: torch.Tensor, q_descale=None,
+                      k_descale=None, cu_seqlens_q=None, cu_seqlens_k=None, seqused_k=None,
+                      block_table=None, return_value: int = 1, workspace=None, out=None):
+    """Runs li_forward; returns (sparse_indices, sparse_values or None)."""
+    st, ws_bytes = li_workspace_size(p)
+    _check(st, "li_workspace_size")
+    dev = q.device
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if p.layout_q == LAYOUT["TND"]:
+        oshape = (p.total_q, 1, p.topk)
+    else:
+        oshape = (p.batch, p.max_seqlen_q, 1, p.topk)
+    if out is None:
+        idx = torch.empty(oshape, dtype=torch.int32, device=dev)
+        val = torch.empty(oshape, dtype=torch.float32, device=dev) if return_value else None
+    else:
+        idx, val = out
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(li_forward(p, _ptr(q), _ptr(k), _ptr(w), _ptr(q_descale), _ptr(k_descale),
+                      _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(seqused_k), _ptr(block_table),
+                      metadata.data_ptr(), _ptr(workspace), wsb, idx.data_ptr(), _ptr(val),
+                      stream), "li_forward")
+    return idx, val
+
+
+def run_instance(inst: dict, device="cuda", return_value: int = 1):
+    """Convenience: runs metadata + forward on a synth-style instance dict (CPU
+    tensors are copied to `device`).  Returns (indices, values) on the device."""
+    dev = torch.device(device)
+    g = {n: (inst[n].to(dev) if isinstance(inst.get(n), torch.Tensor) else None)
+         for n in ("q", "k", "w", "q_descale", "k_descale", "cu_seqlens_q", "cu_seqlens_k",
+                   "seqused_k", "block_table")}
+    if inst["layout_k"] == "PA_BSND":
+        # keep the pool's block stride: copy the whole padded pool, then view it
+        kc = inst["k"]
+        base = kc.as_strided((kc.shape[0], kc.stride(0)), (kc.stride(0), 1))
+        pool = base.to(dev)
+        g["k"] = pool.as_strided(kc.shape, kc.stride())
+    p = problem_for(inst, g["k"])
+    meta = lightning_indexer_metadata(p, cu_seqlens_q=g["cu_seqlens_q"],
+                                      cu_seqlens_k=g["cu_seqlens_k"], seqused_k=g["seqused_k"],
+                                      device=dev)
+    return lightning_indexer(p, g["q"], g["k"], g["w"], metadata=meta, q_descale=g["q_descale"],
+                             k_descale=g["k_descale"], cu_seqlens_q=g["cu_seqlens_q"],
+                             cu_seqlens_k=g["cu_seqlens_k"], seqused_k=g["seqused_k"],
+                             block_table=g["block_table"], return_value=return_value)
+
+
+def problem_for(inst: dict, k_dev: Optional[torch.Tensor] = None) -> Problem:
+    """Problem scalars of a synth-style instance dict."""
+    k = inst["k"] if k_dev is None else k_dev
+    return problem_from(inst["q"], k, inst["w"], inst["topk"], layout_q=inst["layout_q"],
+                        layout_k=inst["layout_k"], mask_mode=inst["mask_mode"],
+                        batch_size=inst["batch"], max_seqlen_q=inst["max_seqlen_q"],
+                        max_seqlen_k=inst["max_seqlen_k"], block_table=inst.get("block_table"))

@@ -1,0 +1,262 @@
+// Host side of the C ABI (include/li.h): argument validation, sizing, the
+// launch plan, and the kernel launches.  No device memory is allocated and the
+// host never waits for the device here.
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/li.h"
+#include "li_internal.h"
+
+using namespace li;
+
+namespace {
+
+inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int elem_bytes(int dt) { return dt == LI_DT_FP8_E4M3 ? 1 : (dt == LI_DT_FP32 ? 4 : 2); }
+
+// Scalar checks (no pointers, no HIP).  Ranges from the pages' constraint lists
+// (lightning_indexer page, Constraints; aclnnLightningIndexerV2 page, 约束说明).
+li_status validate_scalars(const li_problem* p) {
+  if (!p) return LI_ERR_INVALID_ARGUMENT;
+  if (p->batch < 0 || p->max_seqlen_q < 0 || p->max_seqlen_k < 0) return LI_ERR_INVALID_ARGUMENT;
+  if (p->num_heads_q < 1 || p->num_heads_q > kMaxHeads) return LI_ERR_INVALID_ARGUMENT;
+  if (p->num_heads_k != 1) return LI_ERR_INVALID_ARGUMENT;
+  if (p->head_dim != kHeadDim) return LI_ERR_INVALID_ARGUMENT;
+  if (p->topk < 1) return LI_ERR_INVALID_ARGUMENT;
+  if (p->topk > kMaxTopk) {
+    // 3072 .. 8192 in steps of 1024 are valid on the pages, not built here
+    if (p->topk <= 8192 && p->topk % 1024 == 0) return LI_ERR_UNSUPPORTED;
+    return LI_ERR_INVALID_ARGUMENT;
+  }
+  if (p->layout_q != LI_LAYOUT_BSND && p->layout_q != LI_LAYOUT_TND) return LI_ERR_INVALID_ARGUMENT;
+  if (p->layout_k != LI_LAYOUT_BSND && p->layout_k != LI_LAYOUT_TND &&
+      p->layout_k != LI_LAYOUT_PA_BSND)
+    return LI_ERR_INVALID_ARGUMENT;
+  if (p->mask_mode != 0 && p->mask_mode != 3) return LI_ERR_INVALID_ARGUMENT;
+  if (p->qk_dtype != LI_DT_BF16 && p->qk_dtype != LI_DT_FP16 && p->qk_dtype != LI_DT_FP8_E4M3)
+    return LI_ERR_INVALID_ARGUMENT;
+  if (p->w_dtype != LI_DT_BF16 && p->w_dtype != LI_DT_FP32) return LI_ERR_INVALID_ARGUMENT;
+  if (p->cmp_ratio < 1) return LI_ERR_INVALID_ARGUMENT;
+  if (p->cmp_ratio != 1) return LI_ERR_UNSUPPORTED;
+  if (p->layout_q == LI_LAYOUT_TND && p->total_q < 0) return LI_ERR_INVALID_ARGUMENT;
+  if (p->layout_k == LI_LAYOUT_TND && p->total_k < 0) return LI_ERR_INVALID_ARGUMENT;
+  if (p->layout_k == LI_LAYOUT_PA_BSND) {
+    if (p->block_size < 1 || p->block_size > 1024) return LI_ERR_INVALID_ARGUMENT;
+    if (((int64_t)p->block_size * kHeadDim * elem_bytes(p->qk_dtype)) % 32 != 0)
+      return LI_ERR_INVALID_ARGUMENT;
+    if (p->num_blocks < 1 || p->max_blocks_per_seq < 1) return LI_ERR_INVALID_ARGUMENT;
+    const int64_t contig = (int64_t)p->block_size * kHeadDim;
+    if (p->k_block_stride != 0 && p->k_block_stride < contig) return LI_ERR_INVALID_ARGUMENT;
+    if ((p->k_block_stride * elem_bytes(p->qk_dtype)) % 16 != 0) return LI_ERR_INVALID_ARGUMENT;
+    if ((int64_t)p->max_seqlen_k > (int64_t)p->max_blocks_per_seq * p->block_size)
+      return LI_ERR_INVALID_ARGUMENT;
+  }
+  // 32-bit token offsets inside the kernels
+  const int64_t rows = p->layout_q == LI_LAYOUT_TND ? p->total_q
+                                                    : (int64_t)p->batch * p->max_seqlen_q;
+  const int64_t keys = p->layout_k == LI_LAYOUT_TND ? p->total_k
+                                                    : (int64_t)p->batch * p->max_seqlen_k;
+  if (rows > INT32_MAX || keys > INT32_MAX) return LI_ERR_UNSUPPORTED;
+  return LI_OK;
+}
+
+int64_t query_rows(const li_problem* p) {
+  return p->layout_q == LI_LAYOUT_TND ? p->total_q : (int64_t)p->batch * p->max_seqlen_q;
+}
+
+// Decode mode: a few query rows per batch and a bounded dense score workspace.
+bool use_decode(const li_problem* p) {
+  if (p->max_seqlen_q > kDecodeMaxRows || p->max_seqlen_k <= 0) return false;
+  const int64_t ws = (int64_t)p->batch * p->max_seqlen_q * align_up(p->max_seqlen_k, 64) * 4;
+  return ws <= (int64_t(1) << 30);
+}
+
+li_status make_plan(const li_problem* p, Plan* pl) {
+  li_status st = validate_scalars(p);
+  if (st != LI_OK) return st;
+  memset(pl, 0, sizeof(*pl));
+  const int B = p->batch;
+  pl->mblocks = p->num_heads_q <= 32 ? 1 : 2;
+  const int rb = kHeadDim * elem_bytes(p->qk_dtype);     // bytes per key row
+  if (use_decode(p)) {
+    pl->mode = kModeDecode;
+    const int64_t keys = (int64_t)B * p->max_seqlen_q * p->max_seqlen_k;
+    int64_t chunk = align_up((size_t)cdiv64(keys, 1024), 256);
+    chunk = std::min<int64_t>(std::max<int64_t>(chunk, 256), 16384);
+    pl->chunk = (int32_t)chunk;
+    const int64_t items = (int64_t)B * p->max_seqlen_q * cdiv64(p->max_seqlen_k, chunk);
+    if (items > INT32_MAX / 16) return LI_ERR_UNSUPPORTED;
+    pl->max_items = (int32_t)items;
+    pl->ws_row_stride = (int64_t)align_up(p->max_seqlen_k, 64);
+    pl->ws_bytes = (size_t)B * p->max_seqlen_q * pl->ws_row_stride * 4;
+    const int cache = std::min(p->max_seqlen_k, kSelectCacheKeys);
+    pl->lds_select = (size_t)(kSelectThreads / 64) * 256 * 4 + 256 + (size_t)cache * 4;
+  } else {
+    pl->mode = kModePrefill;
+    int64_t items;
+    if (p->layout_q == LI_LAYOUT_TND)
+      items = std::min<int64_t>(cdiv64(p->total_q, kRowsPerItem) + B,
+                                (int64_t)B * cdiv64(p->max_seqlen_q, kRowsPerItem));
+    else
+      items = (int64_t)B * cdiv64(p->max_seqlen_q, kRowsPerItem);
+    if (items > INT32_MAX / 16) return LI_ERR_UNSUPPORTED;
+    pl->max_items = (int32_t)items;
+    const size_t fixed = 2 * (size_t)kTileKeys * rb + (size_t)kRowsPerItem * 256 * 4;
+    const int k64 = (int)align_up(p->topk, 64);
+    const int fit = (int)((kLdsBudget - fixed) / (kRowsPerItem * 8) / 64 * 64);
+    int cap = std::max(2 * k64, k64 + 512);
+    cap = std::min(cap, fit);
+    if (cap < k64 + 64) return LI_ERR_UNSUPPORTED;
+    pl->cap = cap;
+    pl->lds_prefill = fixed + (size_t)kRowsPerItem * cap * 8;
+  }
+  pl->off_batch = sizeof(MetaHeader);
+  pl->off_counts = align_up(pl->off_batch + (size_t)B * 16, 16);
+  pl->off_starts = align_up(pl->off_counts + (size_t)B * 4, 16);
+  pl->off_items = align_up(pl->off_starts + (size_t)B * 4, 16);
+  pl->meta_bytes = pl->off_items + (size_t)pl->max_items * 16;
+  if (pl->meta_bytes > (size_t)INT32_MAX) return LI_ERR_UNSUPPORTED;
+  return LI_OK;
+}
+
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+// Pointer presence rules shared by li_metadata and li_forward
+// (aclnnLightningIndexerV2 page, 约束说明: cu_seqlens only with TND layouts,
+// seqused_k required with, and only with, the paged key layout).
+li_status validate_lengths(const li_problem* p, const int32_t* cu_q, const int32_t* cu_k,
+                           const int32_t* seqused_k) {
+  if ((p->layout_q == LI_LAYOUT_TND) != (cu_q != nullptr)) return LI_ERR_INVALID_ARGUMENT;
+  if ((p->layout_k == LI_LAYOUT_TND) != (cu_k != nullptr)) return LI_ERR_INVALID_ARGUMENT;
+  if ((p->layout_k == LI_LAYOUT_PA_BSND) != (seqused_k != nullptr)) return LI_ERR_INVALID_ARGUMENT;
+  return LI_OK;
+}
+
+KArgs base_args(const li_problem* p, const Plan& pl, void* metadata) {
+  KArgs a;
+  memset(&a, 0, sizeof(a));
+  a.meta = static_cast<unsigned char*>(metadata);
+  a.batch = p->batch;
+  a.s1max = p->max_seqlen_q;
+  a.s2max = p->max_seqlen_k;
+  a.n1 = p->num_heads_q;
+  a.topk = p->topk;
+  a.layout_q = p->layout_q;
+  a.layout_k = p->layout_k;
+  a.mask_mode = p->mask_mode;
+  a.block_size = p->block_size;
+  a.max_blocks_per_seq = p->max_blocks_per_seq;
+  a.k_block_stride = p->k_block_stride ? p->k_block_stride : (int64_t)p->block_size * kHeadDim;
+  a.cap = pl.cap;
+  a.chunk = pl.chunk;
+  a.max_items = pl.max_items;
+  a.ws_row_stride = pl.ws_row_stride;
+  a.off_batch = (int32_t)pl.off_batch;
+  a.off_counts = (int32_t)pl.off_counts;
+  a.off_starts = (int32_t)pl.off_starts;
+  a.off_items = (int32_t)pl.off_items;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+li_status li_metadata_size(const li_problem* p, size_t* bytes) {
+  if (!bytes) return LI_ERR_INVALID_ARGUMENT;
+  Plan pl;
+  li_status st = make_plan(p, &pl);
+  if (st != LI_OK) return st;
+  *bytes = pl.meta_bytes;
+  return LI_OK;
+}
+
+li_status li_workspace_size(const li_problem* p, size_t* bytes) {
+  if (!bytes) return LI_ERR_INVALID_ARGUMENT;
+  Plan pl;
+  li_status st = make_plan(p, &pl);
+  if (st != LI_OK) return st;
+  *bytes = pl.ws_bytes;
+  return LI_OK;
+}
+
+li_status li_metadata(const li_problem* p, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                      const int32_t* seqused_k, void* metadata, size_t metadata_bytes,
+                      hipStream_t stream) {
+  Plan pl;
+  li_status st = make_plan(p, &pl);
+  if (st != LI_OK) return st;
+  st = validate_lengths(p, cu_seqlens_q, cu_seqlens_k, seqused_k);
+  if (st != LI_OK) return st;
+  if (!metadata || !aligned(metadata, 16)) return LI_ERR_INVALID_ARGUMENT;
+  if (metadata_bytes < pl.meta_bytes) return LI_ERR_WORKSPACE_TOO_SMALL;
+  if (query_rows(p) == 0) return LI_OK;
+  KArgs a = base_args(p, pl, metadata);
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.seqused_k = seqused_k;
+  return launch_metadata(a, pl.mode, stream) == hipSuccess ? LI_OK : LI_ERR_HIP;
+}
+
+li_status li_forward(const li_problem* p, const void* q, const void* k, const void* w,
+                     const float* q_descale, const float* k_descale, const int32_t* cu_seqlens_q,
+                     const int32_t* cu_seqlens_k, const int32_t* seqused_k,
+                     const int32_t* block_table, const void* metadata, void* workspace,
+                     size_t workspace_bytes, int32_t* sparse_indices, float* sparse_values,
+                     hipStream_t stream) {
+  Plan pl;
+  li_status st = make_plan(p, &pl);
+  if (st != LI_OK) return st;
+  st = validate_lengths(p, cu_seqlens_q, cu_seqlens_k, seqused_k);
+  if (st != LI_OK) return st;
+  if ((p->layout_k == LI_LAYOUT_PA_BSND) != (block_table != nullptr)) return LI_ERR_INVALID_ARGUMENT;
+  const bool fp8 = p->qk_dtype == LI_DT_FP8_E4M3;
+  if (fp8 != (q_descale != nullptr) || fp8 != (k_descale != nullptr)) return LI_ERR_INVALID_ARGUMENT;
+  if (!q || !k || !w || !metadata || !sparse_indices) return LI_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 16) || !aligned(metadata, 16))
+    return LI_ERR_INVALID_ARGUMENT;
+  if (fp8 && (!aligned(q_descale, 4) || !aligned(k_descale, 4))) return LI_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < pl.ws_bytes) return LI_ERR_WORKSPACE_TOO_SMALL;
+  if (pl.ws_bytes > 0 && (!workspace || !aligned(workspace, 16))) return LI_ERR_INVALID_ARGUMENT;
+  if (query_rows(p) == 0) return LI_OK;
+
+  KArgs a = base_args(p, pl, const_cast<void*>(metadata));
+  a.q = q;
+  a.k = k;
+  a.w = w;
+  a.q_descale = q_descale;
+  a.k_descale = k_descale;
+  a.block_table = block_table;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.seqused_k = seqused_k;
+  a.ws = static_cast<uint32_t*>(workspace);
+  a.out_idx = sparse_indices;
+  a.out_val = sparse_values;
+  const int qk = p->qk_dtype, wt = p->w_dtype;
+  hipError_t e;
+  if (pl.mode == kModePrefill) {
+    e = launch_prefill(a, qk, wt, pl.mblocks, pl.max_items, pl.lds_prefill, stream);
+  } else {
+    e = launch_decode(a, qk, wt, pl.mblocks, pl.max_items, stream);
+    if (e == hipSuccess)
+      e = launch_select(a, p->batch * p->max_seqlen_q, pl.lds_select, stream);
+  }
+  return e == hipSuccess ? LI_OK : LI_ERR_HIP;
+}
+
+const char* li_status_str(li_status s) {
+  switch (s) {
+    case LI_OK: return "LI_OK";
+    case LI_ERR_INVALID_ARGUMENT: return "LI_ERR_INVALID_ARGUMENT";
+    case LI_ERR_UNSUPPORTED: return "LI_ERR_UNSUPPORTED";
+    case LI_ERR_WORKSPACE_TOO_SMALL: return "LI_ERR_WORKSPACE_TOO_SMALL";
+    case LI_ERR_HIP: return "LI_ERR_HIP";
+    default: return "LI_UNKNOWN_STATUS";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Internal definitions shared by the host dispatch (li_host.cpp) and the HIP
+// kernels: the launch plan, the metadata layout and the kernel argument block.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace li {
+
+constexpr int kHeadDim = 128;
+constexpr int kMaxHeads = 64;
+constexpr int kMaxTopk = 2048;
+constexpr int kRowsPerItem = 4;        // prefill: one query row per wave, 4 waves
+constexpr int kTileKeys = 64;          // keys per score tile (two 32-key MFMA column blocks)
+constexpr int kDecodeMaxRows = 4;      // decode mode: at most this many query rows per batch
+constexpr int kSelectThreads = 1024;   // decode-mode select kernel
+constexpr int kSelectCacheKeys = 32768;// decode-mode select: rows up to this length sit in LDS
+constexpr size_t kLdsBudget = 160 * 1024;
+constexpr int kMetaMagic = 0x4C494D44; // "LIMD"
+
+enum Mode : int32_t { kModePrefill = 0, kModeDecode = 1 };
+
+// Metadata buffer layout (all int32 / int4 records, offsets in bytes):
+//   [0, 256)        header, see MetaHeader
+//   batch table     B x int4 {q_tok_off, s1_b, k_tok_off, s2_b}
+//   counts          B x int32  (items per batch)
+//   starts          B x int32  (exclusive prefix of counts)
+//   items           max_items x int4
+//     prefill item: {b, q0, nrows, 0}
+//     decode item : {b, i, k0, k1}
+struct MetaHeader {
+  int32_t n_items;
+  int32_t mode;
+  int32_t chunk;
+  int32_t magic;
+  int32_t batch;
+  int32_t max_items;
+  int32_t pad[58];
+};
+static_assert(sizeof(MetaHeader) == 256, "metadata header is 256 bytes");
+
+struct Plan {
+  int32_t mode;
+  int32_t max_items;
+  int32_t chunk;          // decode: keys per item
+  int32_t cap;            // prefill: candidate slots per row
+  int32_t mblocks;        // 1 (N1 <= 32) or 2 (N1 <= 64)
+  size_t lds_prefill;     // dynamic LDS of the prefill kernel
+  size_t lds_select;      // dynamic LDS of the decode-mode select kernel
+  size_t meta_bytes;
+  size_t off_batch, off_counts, off_starts, off_items;
+  size_t ws_bytes;
+  int64_t ws_row_stride;  // decode: u32 slots per (batch, row) score row
+};
+
+// Kernel argument block (passed by value).
+struct KArgs {
+  const void* q;
+  const void* k;
+  const void* w;
+  const float* q_descale;
+  const float* k_descale;
+  const int32_t* block_table;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* seqused_k;
+  unsigned char* meta;      // metadata base
+  uint32_t* ws;             // decode: dense score rows
+  int32_t* out_idx;
+  float* out_val;
+  int64_t k_block_stride;   // elements between paged blocks
+  int64_t ws_row_stride;
+  int32_t batch, s1max, s2max;
+  int32_t n1, topk;
+  int32_t layout_q, layout_k, mask_mode;
+  int32_t block_size, max_blocks_per_seq;
+  int32_t cap, chunk, max_items;
+  int32_t off_batch, off_counts, off_starts, off_items;
+};
+
+// Layout / dtype codes as in li.h.
+enum { L_BSND = 0, L_TND = 1, L_PA = 2 };
+enum { DT_BF16 = 0, DT_FP8 = 1, DT_FP32 = 2, DT_FP16 = 3 };
+
+// Launchers (defined in the .hip files); return the hipGetLastError() of the launch.
+hipError_t launch_metadata(const KArgs& a, int mode, hipStream_t s);
+hipError_t launch_prefill(const KArgs& a, int qk_dtype, int w_dtype, int mblocks, int grid,
+                          size_t lds, hipStream_t s);
+hipError_t launch_decode(const KArgs& a, int qk_dtype, int w_dtype, int mblocks, int grid,
+                         hipStream_t s);
+hipError_t launch_select(const KArgs& a, int grid, size_t lds, hipStream_t s);
+
+}  // namespace li

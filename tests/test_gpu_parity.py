@@ -1,0 +1,238 @@
+"""HIP path vs the CPU oracle on seeded inputs (needs an MI355X).
+
+Every case runs li_metadata + li_forward through the C ABI, then compares the
+outputs with the oracle row by row (tests/compare.py: exact structure and
+padding, values within 1e-2 * max(1, |I|), index sets equal up to swaps at the
+k-th score).  Small cases are compared on every row; the full-size workloads on
+sampled rows (first / last rows, rows around |V| = k, seeded random rows) and
+structurally on every row.
+"""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from score_top_token_amd import binding, synth
+from tests import compare
+from tests.util import bsnd_inst, int_tensor
+
+pytestmark = pytest.mark.gpu
+
+ORACLE_THREADS = min(16, os.cpu_count() or 1)
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _gpu(inst, return_value=1):
+    _say(f"[gpu] {inst.get('name')} seed={inst.get('seed')} B={inst['batch']} "
+         f"S1={inst['max_seqlen_q']} S2={inst['max_seqlen_k']} N1={inst['n1']} "
+         f"topk={inst['topk']} {inst['layout_q']}/{inst['layout_k']} {inst['qk_dtype']}")
+    idx, val = binding.run_instance(inst, return_value=return_value)
+    torch.cuda.synchronize()
+    topk = inst["topk"]
+    gi = idx.cpu().numpy().reshape(-1, topk)
+    gv = None if val is None else val.cpu().numpy().reshape(-1, topk)
+    return gi, gv
+
+
+def structural_check(gi, gv, inst, ob):
+    """Vectorised checks on every row: valid prefix of exactly min(k, |V|), padding,
+    indices inside the visible window, no duplicates."""
+    topk = inst["topk"]
+    nrows = gi.shape[0]
+    vis = np.empty(nrows, dtype=np.int64)
+    r = 0
+    for b in range(inst["batch"]):
+        s1, s2 = inst["seqlens_q"][b], inst["seqlens_k"][b]
+        i = np.arange(s1)
+        v = np.full(s1, s2) if inst["mask_mode"] == 0 else np.clip(i + s2 - s1 + 1, 0, s2)
+        vis[r:r + s1] = v
+        r += s1
+    assert r == nrows
+    n = np.minimum(vis, topk)
+    valid = gi >= 0
+    assert (valid.sum(1) == n).all(), "number of valid entries"
+    col = np.arange(topk)[None, :]
+    assert (valid == (col < n[:, None])).all(), "valid entries not a prefix"
+    assert ((gi < vis[:, None]) | ~valid).all(), "index outside the visible window"
+    s = np.sort(np.where(valid, gi, -1 - col), axis=1)
+    assert (np.diff(s, axis=1) != 0).all(), "duplicate index"
+    if gv is not None:
+        assert np.isneginf(gv[~valid]).all(), "value padding"
+        assert np.isfinite(gv[valid]).all(), "non-finite value"
+
+
+def compare_all(inst, rows=None, return_value=1, seed_rows=0):
+    gi, gv = _gpu(inst, return_value)
+    ob = oracle.Bound(inst)
+    structural_check(gi, gv, inst, ob)
+    if rows is None:
+        rows = np.arange(gi.shape[0])
+    rows = np.asarray(rows, dtype=np.int64)
+    oi, ov = ob.forward(rows=rows, nthreads=ORACLE_THREADS)
+    rep = compare.check_rows(gi[rows], None if gv is None else gv[rows], oi, ov, rows, ob)
+    _say(f"    rows={rep.rows} max_abs={rep.max_abs:.3g} max_rel={rep.max_rel:.3g} "
+         f"swaps={rep.swaps}")
+    return gi, gv, rep
+
+
+# --------------------------------------------------------------------------
+# small cases, every row compared
+# --------------------------------------------------------------------------
+
+SMALL = {
+    "tiny_s0": ("tiny", 0, {}), "tiny_s1": ("tiny", 1, {}), "tiny_s2": ("tiny", 2, {}),
+    "prefill_700_k64": (None, 3, dict(batch=2, s1=700, s2=700, n1=64, topk=64, w_scale=0.125)),
+    "prefill_700_k256": (None, 4, dict(batch=1, s1=700, s2=700, n1=64, topk=256, w_scale=0.125)),
+    "prefill_k1_mask0": (None, 5, dict(batch=1, s1=130, s2=333, n1=16, topk=1, mask_mode=0)),
+    "heads1_k7": (None, 6, dict(batch=2, s1=77, s2=77, n1=1, topk=7)),
+    "heads33_chunked": (None, 7, dict(batch=1, s1=90, s2=1500, n1=33, topk=100)),
+    "s1_gt_s2": (None, 8, dict(batch=2, s1=200, s2=70, n1=8, topk=32)),
+    "k2048_long": (None, 9, dict(batch=1, s1=24, s2=9000, n1=64, topk=2048, w_scale=0.125)),
+    "w_fp32": (None, 10, dict(batch=1, s1=150, s2=150, n1=20, topk=40, w_dtype="fp32")),
+    "fp16_qk": (None, 11, dict(batch=2, s1=64, s2=32, n1=16, topk=32, qk_dtype="fp16",
+                               w_dtype="fp32")),
+    "fp8_chunked": (None, 12, dict(batch=1, s1=300, s2=2000, n1=64, topk=256, qk_dtype="fp8",
+                                   w_scale=0.125)),
+    "fp8_heads8": (None, 13, dict(batch=2, s1=100, s2=100, n1=8, topk=16, qk_dtype="fp8")),
+    "tnd_small": (None, 14, dict(batch=4, n1=64, topk=128, layout_q="TND", layout_k="TND",
+                                 len_lo=50, len_hi=900, w_scale=0.125)),
+    "tnd_kv_extra": (None, 15, dict(batch=3, n1=12, topk=40, layout_q="TND", layout_k="TND",
+                                    len_lo=5, len_hi=120, kv_extra=37)),
+    "decode_small": (None, 16, dict(batch=5, s1=1, n1=64, topk=128, layout_k="PA_BSND",
+                                    len_lo=300, len_hi=3000, block_size=64, block_pad=5,
+                                    w_scale=0.125)),
+    "decode_rows3": (None, 17, dict(batch=3, s1=3, n1=24, topk=50, layout_k="PA_BSND",
+                                    len_lo=2, len_hi=700, block_size=32)),
+    "decode_fp8": (None, 18, dict(batch=4, s1=2, n1=64, topk=200, layout_k="PA_BSND",
+                                  len_lo=100, len_hi=2500, block_size=128, qk_dtype="fp8",
+                                  w_scale=0.125)),
+    "decode_bsnd_mask0": (None, 19, dict(batch=6, s1=1, s2=5000, n1=64, topk=1000, mask_mode=0,
+                                         w_scale=0.125)),
+    "prefill_paged": (None, 20, dict(batch=2, s1=40, n1=32, topk=64, layout_k="PA_BSND",
+                                     len_lo=300, len_hi=600, block_size=16, block_pad=2)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_case(name):
+    preset, seed, over = SMALL[name]
+    spec = synth.scaled_spec(preset, **over) if preset else synth.Spec(name=name, **over)
+    spec.name = name
+    compare_all(synth.make(spec, seed))
+
+
+def test_return_value_zero_gives_same_indices():
+    inst = synth.make("tiny", 3)
+    gi1, gv1 = _gpu(inst, 1)
+    gi0, gv0 = _gpu(inst, 0)
+    assert gv0 is None
+    assert np.array_equal(gi0, gi1)
+
+
+def test_all_zero_scores_pick_smallest_indices():
+    S, topk = 300, 50
+    q = torch.zeros(1, S, 8, 128).bfloat16()
+    g = torch.Generator().manual_seed(0)
+    k = torch.randn(1, S, 1, 128, generator=g).bfloat16()
+    w = torch.rand(1, S, 8, generator=g).bfloat16()
+    inst = bsnd_inst(q, k, w, topk=topk, mask_mode=3)
+    inst["name"] = "zero_scores"
+    gi, gv = _gpu(inst)
+    for i in range(S):
+        n = min(topk, i + 1)
+        assert list(gi[i, :n]) == list(range(n))
+        assert (gv[i, :n] == 0).all() and not np.signbit(gv[i, :n]).any()
+
+
+def test_integer_scores_exact_with_ties():
+    # small integers: every score is an exact integer in fp32, so the GPU must
+    # equal the oracle exactly, ties at the k-th place included
+    g = torch.Generator().manual_seed(1)
+    B, S, N1, topk = 2, 500, 16, 37
+    q = int_tensor(g, (B, S, N1, 128), -1, 1)
+    k = int_tensor(g, (B, S, 1, 128), -1, 1)
+    w = int_tensor(g, (B, S, N1), -2, 3)
+    inst = bsnd_inst(q, k, w, topk=topk, mask_mode=3)
+    inst["name"] = "integer_ties"
+    gi, gv = _gpu(inst)
+    oi, ov = oracle.Bound(inst).forward(nthreads=ORACLE_THREADS)
+    for r in range(B * S):
+        n = int((oi[r] >= 0).sum())
+        order = np.argsort(gi[r, :n], kind="stable")
+        assert sorted(gi[r, :n].tolist()) == sorted(oi[r, :n].tolist()), f"row {r}"
+        o_map = dict(zip(oi[r, :n].tolist(), ov[r, :n].tolist()))
+        assert all(o_map[s] == v for s, v in zip(gi[r, :n].tolist(), gv[r, :n].tolist()))
+        del order
+
+
+def test_determinism_bitwise():
+    spec = synth.Spec(name="det", batch=1, s1=600, s2=600, n1=64, topk=128, w_scale=0.125)
+    inst = synth.make(spec, 21)
+    a = _gpu(inst)
+    b = _gpu(inst)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    dec = synth.Spec(name="det_dec", batch=3, s1=1, n1=64, topk=256, layout_k="PA_BSND",
+                     len_lo=1000, len_hi=4000, block_size=128, w_scale=0.125)
+    inst = synth.make(dec, 22)
+    a = _gpu(inst)
+    b = _gpu(inst)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+def test_paged_equals_contiguous():
+    spec = synth.Spec(name="pa_eq", batch=3, s1=1, n1=64, topk=300, layout_k="PA_BSND",
+                      len_lo=2000, len_hi=2000, block_size=128, w_scale=0.125)
+    inst = synth.make(spec, 23)
+    bs = inst["block_size"]
+    gi, gv = _gpu(inst)
+    L = inst["seqlens_k"][0]
+    kb = torch.stack([torch.stack([inst["k"][inst["block_table"][b, s // bs], s % bs]
+                                   for s in range(L)]) for b in range(3)])      # [3, L, 1, D]
+    ref = bsnd_inst(inst["q"], kb, inst["w"], topk=300, mask_mode=3)
+    ref["name"] = "pa_eq_ref"
+    ri, rv = _gpu(ref)
+    assert np.array_equal(gi, ri) and np.array_equal(gv, rv)
+
+
+# --------------------------------------------------------------------------
+# the five workloads at full size: sampled rows + structure of every row
+# --------------------------------------------------------------------------
+
+def sample_rows(inst, n_random=24, seed=0):
+    rng = np.random.default_rng(seed)
+    total = sum(inst["seqlens_q"])
+    topk = inst["topk"]
+    rows = {0, total - 1}
+    r = 0
+    for b in range(inst["batch"]):
+        s1, s2 = inst["seqlens_q"][b], inst["seqlens_k"][b]
+        rows.update({r, r + s1 - 1})
+        if inst["mask_mode"] == 3:
+            i_k = topk - 1 - (s2 - s1)          # row whose visible count is exactly k
+            for d in (-1, 0, 1, 2):
+                if 0 <= i_k + d < s1:
+                    rows.add(r + i_k + d)
+        r += s1
+    rows.update(rng.integers(0, total, n_random).tolist())
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name,nrand", [("prefill", 40), ("decode", 12), ("varlen", 12),
+                                        ("longfp8", 4), ("tiny", 0)])
+def test_full_size_config(name, nrand):
+    inst = synth.make(name, 0)
+    rows = None if name == "tiny" else sample_rows(inst, nrand)
+    if name == "decode":
+        rows = rows[:16]
+    if name == "longfp8":
+        rows = [0, 8191, 4000, 123] + rows[:4]
+    compare_all(inst, rows=rows)
