@@ -1,5 +1,5 @@
 // Pieces shared by the score kernels: visible-key limits, key addressing,
-// operand loading and the ReLU / weight / head-sum epilogue.
+// operand loading, K tile staging and the ReLU / weight / head-sum epilogue.
 #pragma once
 
 #include "li_device.h"
@@ -20,22 +20,44 @@ __device__ inline int4 batch_rec(const KArgs& a, int b) {
   return reinterpret_cast<const int4*>(a.meta + a.off_batch)[b];
 }
 
-// Address of the RB-byte row of logical key s of batch b, and its descale slot.
-template <int QK>
-__device__ inline const unsigned char* key_row(const KArgs& a, int b, int k_off, int s,
-                                               int64_t* slot) {
-  constexpr int ES = Mma<QK>::RB / kHeadDim;   // bytes per element
-  const unsigned char* base = reinterpret_cast<const unsigned char*>(a.k);
-  if (a.layout_k == L_PA) {
-    const int lb = s / a.block_size;
-    const int r = s - lb * a.block_size;
-    const int blk = a.block_table[(int64_t)b * a.max_blocks_per_seq + lb];
-    if (slot) *slot = (int64_t)blk * a.block_size + r;
-    return base + ((int64_t)blk * a.k_block_stride + (int64_t)r * kHeadDim) * ES;
+// Logical key s of batch b -> (paged pool block, row).  Power-of-two block
+// sizes use shifts.
+__device__ inline void paged_slot(const KArgs& a, int b, int s, int& blk, int& r) {
+  int lb;
+  if (a.block_shift >= 0) {
+    lb = s >> a.block_shift;
+    r = s & (a.block_size - 1);
+  } else {
+    lb = s / a.block_size;
+    r = s - lb * a.block_size;
   }
-  const int64_t tok = (int64_t)k_off + s;
-  if (slot) *slot = tok;
-  return base + tok * Mma<QK>::RB;
+  blk = a.block_table[(int64_t)b * a.max_blocks_per_seq + lb];
+}
+
+// Address of the RB-byte row of logical key s of batch b.
+template <int QK, bool PAGED>
+__device__ inline const unsigned char* key_row(const KArgs& a, int b, int k_off, int s) {
+  constexpr int RB = Mma<QK>::RB;
+  const unsigned char* base = reinterpret_cast<const unsigned char*>(a.k);
+  if constexpr (PAGED) {
+    int blk, r;
+    paged_slot(a, b, s, blk, r);
+    return base + (int64_t)blk * a.k_block_stride_bytes + (int64_t)r * RB;
+  } else {
+    return base + ((int64_t)k_off + s) * RB;
+  }
+}
+
+// Descale slot of key s (paged: [block, row] of the pool; else the key token).
+template <bool PAGED>
+__device__ inline int64_t key_slot(const KArgs& a, int b, int k_off, int s) {
+  if constexpr (PAGED) {
+    int blk, r;
+    paged_slot(a, b, s, blk, r);
+    return (int64_t)blk * a.block_size + r;
+  } else {
+    return (int64_t)k_off + s;
+  }
 }
 
 template <int WT>
@@ -74,10 +96,46 @@ __device__ inline void load_query(const KArgs& a, int64_t tok, int lane,
     }
 }
 
-// ReLU, per-head weight and head sum of a 64-key tile held as acc[mb][nb]
-// (nb = 32-key column block).  Returns, in lane l, the score of key l of the tile.
-template <int MB>
-__device__ inline float head_sum(const f32x16 (&acc)[MB][2], const float (&wv)[MB][16], int lane) {
+template <int QK, int MB>
+__device__ inline void zero_query(typename Mma<QK>::frag (&qf)[MB][Mma<QK>::KSTEPS],
+                                  float (&wv)[MB][16]) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int j = 0; j < Mma<QK>::KSTEPS; ++j) qf[mb][j] = zero_frag<QK>();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wv[mb][r] = 0.0f;
+  }
+}
+
+// One 64-key score tile of a row: MFMAs over the K tile in LDS (all fragments
+// read first), then ReLU / weight / head sum.  Returns, in lane l, the score of
+// key l of the tile.
+template <int QK, int MB>
+__device__ inline float score_tile_lds(const unsigned char* tile,
+                                       const typename Mma<QK>::frag (&qf)[MB][Mma<QK>::KSTEPS],
+                                       const float (&wv)[MB][16], int lane) {
+  typedef Mma<QK> M;
+  typedef typename M::frag F;
+  F kb[2][M::KSTEPS];
+#pragma unroll
+  for (int j = 0; j < M::KSTEPS; ++j)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) kb[nb][j] = load_frag_lds<QK>(tile, nb * 32 + (lane & 31), lane, j);
+  f32x16 acc[MB][2];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    acc[mb][0] = f32x16{};
+    acc[mb][1] = f32x16{};
+  }
+#pragma unroll
+  for (int j = 0; j < M::KSTEPS; ++j)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = M::mma(qf[mb][j], kb[nb][j], acc[mb][nb]);
+  // ReLU, per-head weight and head sum; lanes 0-31 hold half of the heads of
+  // keys 0-31 (block 0) and 32-63 (block 1), lanes 32-63 the other half.
   float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -86,12 +144,45 @@ __device__ inline float head_sum(const f32x16 (&acc)[MB][2], const float (&wv)[M
       p0 = fmaf(wv[mb][r], fmaxf(acc[mb][0][r], 0.0f), p0);
       p1 = fmaf(wv[mb][r], fmaxf(acc[mb][1][r], 0.0f), p1);
     }
-  // lanes 0-31 hold half of the heads of keys 0-31 (p0) and 32-63 (p1); lanes
-  // 32-63 the other half.  Exchange so lane l ends with the full sum of key l.
   const bool lo = lane < 32;
   const float send = lo ? p1 : p0;
   const float recv = __shfl_xor(send, 32);
   return (lo ? p0 : p1) + recv;
 }
+
+// Cooperative staging of one 64-key K tile: NT threads load it from global
+// memory into registers (16 bytes per chunk) and later store it into LDS in the
+// swizzled layout read by load_frag_lds.  Rows at or beyond kend are zero.
+template <int QK, bool PAGED, int NT>
+struct TileStage {
+  static constexpr int RB = Mma<QK>::RB;
+  static constexpr int NCH = RB / 16;
+  static constexpr int LOADS = kTileKeys * NCH / NT;
+  static_assert(LOADS >= 1 && kTileKeys * NCH % NT == 0, "tile split");
+  i32x4 pre[LOADS];
+
+  __device__ inline void load(const KArgs& a, int b, int k_off, int base, int kend, int tid) {
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+      const int id = tid + NT * r;
+      const int key = id / NCH, c = id % NCH;
+      const int s = base + key;
+      if (s < kend) {
+        const unsigned char* row = key_row<QK, PAGED>(a, b, k_off, s);
+        pre[r] = *reinterpret_cast<const i32x4*>(row + c * 16);
+      } else {
+        pre[r] = i32x4{0, 0, 0, 0};
+      }
+    }
+  }
+  __device__ inline void store(unsigned char* tile, int tid) const {
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+      const int id = tid + NT * r;
+      const int key = id / NCH, c = id % NCH;
+      *reinterpret_cast<i32x4*>(tile + lds_chunk_off<QK>(key, c)) = pre[r];
+    }
+  }
+};
 
 }  // namespace li

@@ -1,32 +1,88 @@
 // Decode-shaped problems (at most a few query rows per batch, long key lists).
 //
-// A handful of query rows cannot fill 256 compute units row by row, so the keys
-// of each row are cut into chunks (the work items of the metadata kernel).  The
-// split kernel streams each chunk of K from HBM once, straight into MFMA B
-// operands (no LDS round trip: every K byte is used by one row only), applies
-// the ReLU / weight / head-sum epilogue, and stores each key's score as an
-// order-preserving u32 into a dense per-row slot array in the workspace.  The
-// select kernel then runs one workgroup per row: an exact 8-bit-digit radix
-// select of the k-th largest key over the row (held in LDS when it fits), and
-// a stable, block-wide compaction that writes the top-k in increasing key
-// order, ties resolved toward smaller indices, and pads with -1 / -inf.
+// A handful of query rows cannot fill 256 compute units row by row, so the
+// visible keys of all rows are cut into segments of about equal length (the
+// work items of the metadata kernel).  The split kernel streams each segment of
+// K from HBM once, straight into MFMA B operands (every K byte is used by one
+// row only, so there is no LDS round trip), double-buffered in registers so the
+// next tile's loads are in flight while the current tile is scored, applies the
+// ReLU / weight / head-sum epilogue and stores each key's score into a dense
+// per-row fp32 array in the workspace.  The select kernel then runs one
+// workgroup per row: the exact bucket select of the k-th element (value
+// descending, smaller key first on ties) over the row held in LDS, and a stable
+// write of the top-k in ascending key order, padded with -1 / -inf.
 //
 // The score follows the npu_lightning_indexer_pto page (formula under "功能说明")
 // and the lightning_indexer page ("Function" steps 1-3, Constraints for the
 // padding); paged keys are read through block_table (npu_lightning_indexer_pto
 // page, block_table parameter).
 #include "li_common_kernels.h"
+#include "li_select.h"
 
 namespace li {
 
 namespace {
 
-constexpr int kSplitWaves = 4;
+template <int QK, bool PAGED>
+__device__ inline void load_key_frags(const KArgs& a, int b, int k_off, int base, int k1, int lane,
+                                      typename Mma<QK>::frag (&kf)[2][Mma<QK>::KSTEPS],
+                                      int64_t& slot) {
+  typedef Mma<QK> M;
+  slot = 0;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int s = base + nb * 32 + (lane & 31);
+    if (s < k1) {
+      const unsigned char* row = key_row<QK, PAGED>(a, b, k_off, s);
+#pragma unroll
+      for (int j = 0; j < M::KSTEPS; ++j) kf[nb][j] = load_frag_global<QK>(row + frag_off<QK>(lane, j));
+      // lane l reports key base + l: column l % 32 of block l / 32
+      if constexpr (QK == DT_FP8) {
+        if (nb == (lane >> 5)) slot = key_slot<PAGED>(a, b, k_off, s);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < M::KSTEPS; ++j) kf[nb][j] = zero_frag<QK>();
+    }
+  }
+}
 
-template <int QK, int MB, int WT>
-__global__ __launch_bounds__(256, 2) void split_kernel(KArgs a) {
+template <int QK, int MB>
+__device__ inline float score_tile_regs(const typename Mma<QK>::frag (&qf)[MB][Mma<QK>::KSTEPS],
+                                        const typename Mma<QK>::frag (&kf)[2][Mma<QK>::KSTEPS],
+                                        const float (&wv)[MB][16], int lane) {
+  typedef Mma<QK> M;
+  f32x16 acc[MB][2];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    acc[mb][0] = f32x16{};
+    acc[mb][1] = f32x16{};
+  }
+#pragma unroll
+  for (int j = 0; j < M::KSTEPS; ++j)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = M::mma(qf[mb][j], kf[nb][j], acc[mb][nb]);
+  float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p0 = fmaf(wv[mb][r], fmaxf(acc[mb][0][r], 0.0f), p0);
+      p1 = fmaf(wv[mb][r], fmaxf(acc[mb][1][r], 0.0f), p1);
+    }
+  const bool lo = lane < 32;
+  const float send = lo ? p1 : p0;
+  const float recv = __shfl_xor(send, 32);
+  return (lo ? p0 : p1) + recv;
+}
+
+template <int QK, int MB, int WT, bool PAGED>
+__global__ __launch_bounds__(kDecodeWaves * 64, 1) void split_kernel(KArgs a) {
   typedef Mma<QK> M;
   typedef typename M::frag F;
+  constexpr int STEP = kDecodeWaves * kTileKeys;
   const MetaHeader* hdr = reinterpret_cast<const MetaHeader*>(a.meta);
   if ((int)blockIdx.x >= hdr->n_items) return;
   const int4 item = reinterpret_cast<const int4*>(a.meta + a.off_items)[blockIdx.x];
@@ -38,89 +94,304 @@ __global__ __launch_bounds__(256, 2) void split_kernel(KArgs a) {
   F qf[MB][M::KSTEPS];
   float wv[MB][16];
   load_query<QK, MB, WT>(a, tok, lane, qf, wv);
+  float* dst = a.ws + ((int64_t)b * a.s1max + i) * a.ws_row_stride;
 
-  uint32_t* dst = a.ws + ((int64_t)b * a.s1max + i) * a.ws_row_stride;
-  for (int base = k0 + wave * kTileKeys; base < k1; base += kSplitWaves * kTileKeys) {
-    F kf[2][M::KSTEPS];
-    int64_t slot[2] = {0, 0};
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int s = base + nb * 32 + (lane & 31);
-      if (s < k1) {
-        const unsigned char* row = key_row<QK>(a, b, br.z, s, &slot[nb]);
-#pragma unroll
-        for (int j = 0; j < M::KSTEPS; ++j) kf[nb][j] = load_frag_global<QK>(row + frag_off<QK>(lane, j));
-      } else {
-#pragma unroll
-        for (int j = 0; j < M::KSTEPS; ++j) kf[nb][j] = zero_frag<QK>();
-      }
-    }
-    f32x16 acc[MB][2];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      acc[mb][0] = f32x16{};
-      acc[mb][1] = f32x16{};
-    }
-#pragma unroll
-    for (int j = 0; j < M::KSTEPS; ++j)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = M::mma(qf[mb][j], kf[nb][j], acc[mb][nb]);
-    float tot = head_sum<MB>(acc, wv, lane);
+  auto finish = [&](int base, float tot, int64_t slot) {
     const int s = base + lane;
     if (s < k1) {
-      if constexpr (QK == DT_FP8) {
-        // both lane halves load every key of the tile, so lane l already holds the
-        // slot of its own key (column l % 32 of block l / 32)
-        tot *= a.k_descale[lane < 32 ? slot[0] : slot[1]];
-      }
-      dst[s] = f2key(tot);
+      if constexpr (QK == DT_FP8) tot *= a.k_descale[slot];
+      dst[s] = tot == 0.0f ? 0.0f : tot;
     }
+  };
+
+  F ka[2][M::KSTEPS], kb[2][M::KSTEPS];
+  int64_t sa = 0, sb = 0;
+  int base = k0 + wave * kTileKeys;
+  if (base < k1) load_key_frags<QK, PAGED>(a, b, br.z, base, k1, lane, ka, sa);
+  while (base < k1) {
+    if (base + STEP < k1) load_key_frags<QK, PAGED>(a, b, br.z, base + STEP, k1, lane, kb, sb);
+    finish(base, score_tile_regs<QK, MB>(qf, ka, wv, lane), sa);
+    base += STEP;
+    if (base >= k1) break;
+    if (base + STEP < k1) load_key_frags<QK, PAGED>(a, b, br.z, base + STEP, k1, lane, ka, sa);
+    finish(base, score_tile_regs<QK, MB>(qf, kb, wv, lane), sb);
+    base += STEP;
   }
 }
 
-// ---- block-wide helpers for the select kernel (1024 threads = 16 waves) ----
-
+// ---------------------------------------------------------------------------
+// block-wide helpers of the select kernel (1024 threads = 16 waves)
+// ---------------------------------------------------------------------------
 constexpr int kSelWaves = kSelectThreads / 64;
+constexpr int kNB = kSelectBuckets;
 
-// exclusive prefix sum over the block; `tmp` holds kSelWaves ints of LDS
-__device__ inline int block_exclusive_scan(int v, int* tmp, int* total) {
-  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int incl = wave_prefix_sum(v);
-  if (l == 63) tmp[wave] = incl;
+struct SelShared {
+  int misc[64];           // 0: bucket, 1: above, 2: count, 3: gathered, 4..5: fb/eb, 8..: scan
+  float cand_f[kSelSmall];
+  uint32_t cand_e[kSelSmall];
+  uint32_t hist[kNB];
+};
+
+__device__ inline float block_min_f(float v, int* tmp) {
+  v = wave_min_f(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) tmp[w] = __float_as_int(v);
   __syncthreads();
-  int wbase = 0, all = 0;
-  for (int w = 0; w < kSelWaves; ++w) {
-    const int t = tmp[w];
-    if (w < wave) wbase += t;
+  float r = __int_as_float(tmp[0]);
+  for (int x = 1; x < kSelWaves; ++x) r = fminf(r, __int_as_float(tmp[x]));
+  __syncthreads();
+  return r;
+}
+__device__ inline float block_max_f(float v, int* tmp) {
+  v = wave_max_f(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) tmp[w] = __float_as_int(v);
+  __syncthreads();
+  float r = __int_as_float(tmp[0]);
+  for (int x = 1; x < kSelWaves; ++x) r = fmaxf(r, __int_as_float(tmp[x]));
+  __syncthreads();
+  return r;
+}
+__device__ inline uint32_t block_min_u(uint32_t v, int* tmp) {
+  v = wave_min_u(v);
+  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = (int)v;
+  __syncthreads();
+  uint32_t r = (uint32_t)tmp[0];
+  for (int x = 1; x < kSelWaves; ++x) r = min(r, (uint32_t)tmp[x]);
+  __syncthreads();
+  return r;
+}
+__device__ inline uint32_t block_max_u(uint32_t v, int* tmp) {
+  v = wave_max_u(v);
+  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = (int)v;
+  __syncthreads();
+  uint32_t r = (uint32_t)tmp[0];
+  for (int x = 1; x < kSelWaves; ++x) r = max(r, (uint32_t)tmp[x]);
+  __syncthreads();
+  return r;
+}
+
+// exclusive prefix over the 16 waves of a per-wave (uniform) value
+__device__ inline int block_wave_prefix(int v, int* tmp, int* total) {
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) tmp[w] = v;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int x = 0; x < kSelWaves; ++x) {
+    const int t = tmp[x];
+    before += x < w ? t : 0;
     all += t;
   }
   __syncthreads();
   if (total) *total = all;
-  return wbase + incl - v;
+  return before;
+}
+
+// Bucket of the element of rank r from the top of hist[0, kNB): thread t owns
+// buckets 2t, 2t+1.  Writes bucket / above / count to sh.misc[0..2].
+__device__ inline void block_find_bucket(SelShared& sh, int r) {
+  const int t = threadIdx.x, w = t >> 6;
+  const uint32_t h0 = sh.hist[2 * t], h1 = sh.hist[2 * t + 1];
+  const int s = (int)(h0 + h1);
+  const int wsuf = wave_suffix_sum(s);                 // within the wave
+  if ((t & 63) == 0) sh.misc[8 + w] = wsuf;            // wave total (lane 0 holds the full sum)
+  __syncthreads();
+  int higher = 0;
+  for (int x = w + 1; x < kSelWaves; ++x) higher += sh.misc[8 + x];
+  const int suf = wsuf + higher;
+  const int ab = suf - s;
+  if (ab < r && r <= suf) {
+    if (ab + (int)h1 >= r) {
+      sh.misc[0] = 2 * t + 1;
+      sh.misc[1] = ab;
+      sh.misc[2] = (int)h1;
+    } else {
+      sh.misc[0] = 2 * t;
+      sh.misc[1] = ab + (int)h1;
+      sh.misc[2] = (int)h0;
+    }
+  }
+  __syncthreads();
+}
+
+struct FBucketN {
+  float lo2, scale;
+  __device__ FBucketN(float lo, float hi) {
+    lo2 = lo * 0.5f;
+    scale = fminf((float)kNB / (hi * 0.5f - lo2), 3.0e38f);
+  }
+  __device__ uint32_t operator()(float f) const {
+    const float x = fminf((f * 0.5f - lo2) * scale, (float)(kNB - 1));
+    return (uint32_t)fmaxf(x, 0.0f);
+  }
+};
+
+struct UBucketN {
+  uint32_t ulo;
+  int shift;
+  __device__ UBucketN(uint32_t lo, uint32_t hi) : ulo(lo) {
+    const uint32_t span = hi - lo;
+    const int bits = span ? 32 - __clz(span) : 0;
+    shift = bits > 11 ? bits - 11 : 0;
+  }
+  __device__ uint32_t operator()(uint32_t u) const {
+    const uint32_t b = (u - ulo) >> shift;
+    return b > (uint32_t)(kNB - 1) ? (uint32_t)(kNB - 1) : b;
+  }
+};
+
+// gathers the (<= kSelSmall) candidates with in(f) into sh.cand_*, then wave 0
+// ranks them; the k-th element lands in sh.misc[4..5]
+template <class Pred>
+__device__ inline void block_gather_rank(SelShared& sh, const float* vals, int n, int r, Pred in) {
+  if (threadIdx.x == 0) sh.misc[3] = 0;
+  __syncthreads();
+  for (int e = threadIdx.x; e < n; e += kSelectThreads) {
+    const float f = vals[e];
+    if (in(f)) {
+      const int slot = atomicAdd(&sh.misc[3], 1);
+      if (slot < kSelSmall) {
+        sh.cand_f[slot] = f;
+        sh.cand_e[slot] = (uint32_t)e;
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int m = min(sh.misc[3], kSelSmall);
+    const int l = threadIdx.x;
+    const float cf = l < m ? sh.cand_f[l] : 0.0f;
+    const uint32_t ce = l < m ? sh.cand_e[l] : 0u;
+    float fb;
+    uint32_t eb;
+    wave_rank_small(cf, ce, m, r, fb, eb);
+    if (l == 0) {
+      sh.misc[4] = __float_as_int(fb);
+      sh.misc[5] = (int)eb;
+    }
+  }
+  __syncthreads();
+}
+
+// the r-th entry (index order) whose key equals u; writes fb / eb into sh.misc[4..5]
+__device__ inline void block_rth_equal(SelShared& sh, const float* vals, int n, int r, uint32_t u) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int seg = ((n + kSelWaves - 1) / kSelWaves + 63) / 64 * 64;
+  const int e0 = w * seg, e1 = min(n, e0 + seg);
+  int cnt = 0;
+  for (int p0 = e0; p0 < e1; p0 += 64) {
+    const int p = p0 + l;
+    cnt += __popcll(ballot(p < e1 && f2key(vals[p]) == u));
+  }
+  const int before = block_wave_prefix(cnt, sh.misc + 8, nullptr);
+  if (before < r && r <= before + cnt) {
+    int seen = before;
+    for (int p0 = e0; p0 < e1; p0 += 64) {
+      const int p = p0 + l;
+      const bool eq = p < e1 && f2key(vals[p]) == u;
+      const uint64_t m = ballot(eq);
+      if (seen + __popcll(m) >= r) {
+        if (eq && seen + mbcnt(m) == r - 1) {
+          sh.misc[4] = (int)u;
+          sh.misc[5] = p;
+        }
+        break;
+      }
+      seen += __popcll(m);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) sh.misc[4] = __float_as_int(key2f(u));
+  __syncthreads();
+}
+
+// k-th element of vals[0, n) in (value desc, index asc) order -> sh.misc[4..5]
+__device__ void block_kth(SelShared& sh, const float* vals, int n, int k, float lo, float hi) {
+  int r = k;
+  uint32_t ulo, uhi;
+  if (lo < hi) {
+    const FBucketN fbk(lo, hi);
+    for (int x = threadIdx.x; x < kNB; x += kSelectThreads) sh.hist[x] = 0;
+    __syncthreads();
+    for (int e = threadIdx.x; e < n; e += kSelectThreads) atomicAdd(&sh.hist[fbk(vals[e])], 1u);
+    __syncthreads();
+    block_find_bucket(sh, r);
+    const uint32_t B = (uint32_t)sh.misc[0];
+    const int above = sh.misc[1], cnt = sh.misc[2];
+    r -= above;
+    __syncthreads();
+    if (cnt <= kSelSmall) {
+      block_gather_rank(sh, vals, n, r, [&](float f) { return fbk(f) == B; });
+      return;
+    }
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int e = threadIdx.x; e < n; e += kSelectThreads) {
+      const float f = vals[e];
+      if (fbk(f) == B) {
+        const uint32_t u = f2key(f);
+        mn = min(mn, u);
+        mx = max(mx, u);
+      }
+    }
+    ulo = block_min_u(mn, sh.misc + 8);
+    uhi = block_max_u(mx, sh.misc + 8);
+  } else {
+    ulo = uhi = f2key(lo);
+  }
+  for (;;) {
+    if (ulo == uhi) {
+      block_rth_equal(sh, vals, n, r, ulo);
+      return;
+    }
+    const UBucketN ubk(ulo, uhi);
+    for (int x = threadIdx.x; x < kNB; x += kSelectThreads) sh.hist[x] = 0;
+    __syncthreads();
+    for (int e = threadIdx.x; e < n; e += kSelectThreads) {
+      const uint32_t u = f2key(vals[e]);
+      if (u >= ulo && u <= uhi) atomicAdd(&sh.hist[ubk(u)], 1u);
+    }
+    __syncthreads();
+    block_find_bucket(sh, r);
+    const int B = sh.misc[0], above = sh.misc[1], cnt = sh.misc[2];
+    r -= above;
+    __syncthreads();
+    const uint32_t nlo = ulo + ((uint32_t)B << ubk.shift);
+    uint32_t nhi = (B == kNB - 1) ? uhi : nlo + ((1u << ubk.shift) - 1u);
+    if (nhi > uhi) nhi = uhi;
+    if (cnt <= kSelSmall && nlo != nhi) {
+      block_gather_rank(sh, vals, n, r, [&](float f) {
+        const uint32_t u = f2key(f);
+        return u >= nlo && u <= nhi;
+      });
+      return;
+    }
+    ulo = nlo;
+    uhi = nhi;
+  }
 }
 
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(KArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  SelShared& sh = *reinterpret_cast<SelShared*>(smem);
+  float* cache = reinterpret_cast<float*>(smem + sizeof(SelShared));
   const int r = blockIdx.x;
   const int b = r / a.s1max, i = r - (r / a.s1max) * a.s1max;
   if (b >= a.batch) return;
   const int4 br = batch_rec(a, b);
   if (i >= br.y) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int lim = visible_limit(a.mask_mode, i, br.y, br.w);
   const int topk = a.topk;
   const int64_t tok = (int64_t)br.x + i;
   int32_t* oi = a.out_idx + tok * topk;
   float* ov = a.out_val ? a.out_val + tok * topk : nullptr;
-  const uint32_t* src = a.ws + ((int64_t)b * a.s1max + i) * a.ws_row_stride;
+  const float* src = a.ws + ((int64_t)b * a.s1max + i) * a.ws_row_stride;
 
   if (lim <= topk) {
     for (int e = tid; e < topk; e += kSelectThreads) {
       if (e < lim) {
         oi[e] = e;
-        if (ov) ov[e] = key2f(src[e]);
+        if (ov) ov[e] = src[e];
       } else {
         oi[e] = -1;
         if (ov) ov[e] = -__builtin_inff();
@@ -128,122 +399,89 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(KArgs a) {
     }
     return;
   }
-
-  uint32_t* whist = reinterpret_cast<uint32_t*>(smem);                // kSelWaves x 256
-  int* scratch = reinterpret_cast<int*>(smem + kSelWaves * 256 * 4);   // 64 ints
-  uint32_t* cache = reinterpret_cast<uint32_t*>(smem + kSelWaves * 256 * 4 + 256);
   const bool cached = lim <= kSelectCacheKeys;
-  const uint32_t* keys = src;
-  if (cached) {
-    for (int e = tid; e < lim; e += kSelectThreads) cache[e] = src[e];
-    keys = cache;
+  float mn = __builtin_inff(), mx = -__builtin_inff();
+  for (int e = tid; e < lim; e += kSelectThreads) {
+    const float f = src[e];
+    if (cached) cache[e] = f;
+    mn = fminf(mn, f);
+    mx = fmaxf(mx, f);
   }
+  const float lo = block_min_f(mn, sh.misc + 8);
+  const float hi = block_max_f(mx, sh.misc + 8);
+  const float* vals = cached ? cache : src;
+  block_kth(sh, vals, lim, topk, lo, hi);
+  const float fb = __int_as_float(sh.misc[4]);
+  const uint32_t eb = (uint32_t)sh.misc[5];
+  __syncthreads();
 
-  uint32_t prefix = 0, pmask = 0;
-  int rem = topk;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int x = tid; x < kSelWaves * 256; x += kSelectThreads) whist[x] = 0;
-    __syncthreads();
-    uint32_t* mine = whist + wave * 256;
-    for (int e = tid; e < lim; e += kSelectThreads) {
-      const uint32_t u = keys[e];
-      if ((u & pmask) == prefix) atomicAdd(&mine[(u >> shift) & 255u], 1u);
+  // stable write: each wave owns a contiguous, 64-aligned segment of the row
+  const int seg = ((lim + kSelWaves - 1) / kSelWaves + 63) / 64 * 64;
+  const int e0 = w * seg, e1 = min(lim, e0 + seg);
+  int kept = 0;
+  for (int p0 = e0; p0 < e1; p0 += 64) {
+    const int p = p0 + l;
+    bool keep = false;
+    if (p < e1) {
+      const float f = vals[p];
+      keep = f > fb || (f == fb && (uint32_t)p <= eb);
     }
-    __syncthreads();
-    if (wave == 0) {
-      uint32_t h[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t t = 0;
-        for (int w = 0; w < kSelWaves; ++w) t += whist[w * 256 + 4 * lane + q];
-        h[q] = t;
-      }
-      const int s = (int)(h[0] + h[1] + h[2] + h[3]);
-      const int suf = wave_suffix_sum(s);
-      const int above = suf - s;
-      if (above < rem && rem <= suf) {
-        int acc = above, dgt = 4 * lane, gt = 0;
-        bool done = false;
-        for (int q = 3; q >= 0 && !done; --q) {
-          if (acc + (int)h[q] >= rem) {
-            dgt = 4 * lane + q;
-            gt = acc;
-            done = true;
-          } else {
-            acc += (int)h[q];
-          }
-        }
-        scratch[0] = dgt;
-        scratch[1] = gt;
-      }
-    }
-    __syncthreads();
-    const int dgt = scratch[0], gt = scratch[1];
-    rem -= gt;
-    prefix |= ((uint32_t)dgt) << shift;
-    pmask |= 0xFFu << shift;
-    __syncthreads();
+    kept += __popcll(ballot(keep));
   }
-  const uint32_t kth = prefix;
-  const int ties_needed = rem;
-
-  // stable block-wide compaction: each thread owns a contiguous segment
-  const int seg = (lim + kSelectThreads - 1) / kSelectThreads;
-  const int e0 = tid * seg;
-  const int e1 = e0 + seg < lim ? e0 + seg : lim;
-  int ngt = 0, neq = 0;
-  for (int e = e0; e < e1; ++e) {
-    const uint32_t u = keys[e];
-    ngt += u > kth;
-    neq += u == kth;
-  }
-  const int eq_before = block_exclusive_scan(neq, scratch + 2, nullptr);
-  int my_ties = ties_needed - eq_before;
-  my_ties = my_ties < 0 ? 0 : (my_ties > neq ? neq : my_ties);
-  const int pos0 = block_exclusive_scan(ngt + my_ties, scratch + 2 + kSelWaves, nullptr);
-  int pos = pos0, tl = my_ties;
-  for (int e = e0; e < e1; ++e) {
-    const uint32_t u = keys[e];
-    bool keep = u > kth;
-    if (!keep && u == kth && tl > 0) {
-      keep = true;
-      --tl;
+  int pos = block_wave_prefix(kept, sh.misc + 8, nullptr);
+  for (int p0 = e0; p0 < e1; p0 += 64) {
+    const int p = p0 + l;
+    float f = 0.0f;
+    bool keep = false;
+    if (p < e1) {
+      f = vals[p];
+      keep = f > fb || (f == fb && (uint32_t)p <= eb);
     }
+    const uint64_t m = ballot(keep);
     if (keep) {
-      oi[pos] = e;
-      if (ov) ov[pos] = key2f(u);
-      ++pos;
+      const int o = pos + mbcnt(m);
+      oi[o] = p;
+      if (ov) ov[o] = f;
     }
+    pos += __popcll(m);
   }
-  (void)lane;
 }
 
-template <int QK, int MB, int WT>
+template <int QK, int MB, int WT, bool PAGED>
 hipError_t launch_split(const KArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((split_kernel<QK, MB, WT>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((split_kernel<QK, MB, WT, PAGED>), dim3(grid), dim3(kDecodeWaves * 64), 0, s, a);
   return hipGetLastError();
 }
 
+template <int QK, int MB, int WT>
+hipError_t launch_split_p(const KArgs& a, bool paged, int grid, hipStream_t s) {
+  return paged ? launch_split<QK, MB, WT, true>(a, grid, s)
+               : launch_split<QK, MB, WT, false>(a, grid, s);
+}
+
 template <int QK, int MB>
-hipError_t launch_split_w(const KArgs& a, int w_dtype, int grid, hipStream_t s) {
-  return w_dtype == DT_FP32 ? launch_split<QK, MB, DT_FP32>(a, grid, s)
-                            : launch_split<QK, MB, DT_BF16>(a, grid, s);
+hipError_t launch_split_w(const KArgs& a, int w_dtype, bool paged, int grid, hipStream_t s) {
+  return w_dtype == DT_FP32 ? launch_split_p<QK, MB, DT_FP32>(a, paged, grid, s)
+                            : launch_split_p<QK, MB, DT_BF16>(a, paged, grid, s);
 }
 
 template <int QK>
-hipError_t launch_split_mb(const KArgs& a, int w_dtype, int mblocks, int grid, hipStream_t s) {
-  return mblocks == 1 ? launch_split_w<QK, 1>(a, w_dtype, grid, s)
-                      : launch_split_w<QK, 2>(a, w_dtype, grid, s);
+hipError_t launch_split_mb(const KArgs& a, int w_dtype, int mblocks, bool paged, int grid,
+                           hipStream_t s) {
+  return mblocks == 1 ? launch_split_w<QK, 1>(a, w_dtype, paged, grid, s)
+                      : launch_split_w<QK, 2>(a, w_dtype, paged, grid, s);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const KArgs& a, int qk_dtype, int w_dtype, int mblocks, int grid,
-                         hipStream_t s) {
+size_t select_shared_bytes() { return sizeof(SelShared); }
+
+hipError_t launch_decode(const KArgs& a, int qk_dtype, int w_dtype, int mblocks, bool paged,
+                         int grid, hipStream_t s) {
   switch (qk_dtype) {
-    case DT_BF16: return launch_split_mb<DT_BF16>(a, w_dtype, mblocks, grid, s);
-    case DT_FP16: return launch_split_mb<DT_FP16>(a, w_dtype, mblocks, grid, s);
-    case DT_FP8: return launch_split_mb<DT_FP8>(a, w_dtype, mblocks, grid, s);
+    case DT_BF16: return launch_split_mb<DT_BF16>(a, w_dtype, mblocks, paged, grid, s);
+    case DT_FP16: return launch_split_mb<DT_FP16>(a, w_dtype, mblocks, paged, grid, s);
+    case DT_FP8: return launch_split_mb<DT_FP8>(a, w_dtype, mblocks, paged, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -74,45 +74,54 @@ bool use_decode(const li_problem* p) {
   return ws <= (int64_t(1) << 30);
 }
 
+int64_t prefill_items(const li_problem* p, int rows) {
+  if (p->layout_q == LI_LAYOUT_TND)
+    return std::min<int64_t>(cdiv64(p->total_q, rows) + p->batch,
+                             (int64_t)p->batch * cdiv64(p->max_seqlen_q, rows));
+  return (int64_t)p->batch * cdiv64(p->max_seqlen_q, rows);
+}
+
 li_status make_plan(const li_problem* p, Plan* pl) {
   li_status st = validate_scalars(p);
   if (st != LI_OK) return st;
   memset(pl, 0, sizeof(*pl));
   const int B = p->batch;
   pl->mblocks = p->num_heads_q <= 32 ? 1 : 2;
-  const int rb = kHeadDim * elem_bytes(p->qk_dtype);     // bytes per key row
+  const size_t rb = (size_t)kHeadDim * elem_bytes(p->qk_dtype);     // bytes per key row
+  const size_t tile = (size_t)kTileKeys * rb;
+  const int64_t dcap = (int64_t)align_up(std::max(p->max_seqlen_k, 1), 64);
+  const size_t dense_r0 = std::max(tile, (size_t)kDenseWaves * kWaveScratch);
+  const size_t dense_lds = dense_r0 + (size_t)kDenseWaves * dcap * 4;
+  int64_t items;
   if (use_decode(p)) {
     pl->mode = kModeDecode;
-    const int64_t keys = (int64_t)B * p->max_seqlen_q * p->max_seqlen_k;
-    int64_t chunk = align_up((size_t)cdiv64(keys, 1024), 256);
-    chunk = std::min<int64_t>(std::max<int64_t>(chunk, 256), 16384);
-    pl->chunk = (int32_t)chunk;
-    const int64_t items = (int64_t)B * p->max_seqlen_q * cdiv64(p->max_seqlen_k, chunk);
-    if (items > INT32_MAX / 16) return LI_ERR_UNSUPPORTED;
-    pl->max_items = (int32_t)items;
+    pl->chunk = 256;                      // minimum segment; the device picks the real one
+    items = (int64_t)B * p->max_seqlen_q + kDecodeSegments;
     pl->ws_row_stride = (int64_t)align_up(p->max_seqlen_k, 64);
     pl->ws_bytes = (size_t)B * p->max_seqlen_q * pl->ws_row_stride * 4;
     const int cache = std::min(p->max_seqlen_k, kSelectCacheKeys);
-    pl->lds_select = (size_t)(kSelectThreads / 64) * 256 * 4 + 256 + (size_t)cache * 4;
+    pl->lds_select = select_shared_bytes() + (size_t)cache * 4;
+  } else if (dense_lds <= kLdsBudget) {
+    pl->mode = kModeDense;
+    pl->rows_per_item = kDenseWaves;
+    pl->dcap = (int32_t)dcap;
+    pl->lds_prefill = dense_lds;
+    items = prefill_items(p, kDenseWaves);
   } else {
-    pl->mode = kModePrefill;
-    int64_t items;
-    if (p->layout_q == LI_LAYOUT_TND)
-      items = std::min<int64_t>(cdiv64(p->total_q, kRowsPerItem) + B,
-                                (int64_t)B * cdiv64(p->max_seqlen_q, kRowsPerItem));
-    else
-      items = (int64_t)B * cdiv64(p->max_seqlen_q, kRowsPerItem);
-    if (items > INT32_MAX / 16) return LI_ERR_UNSUPPORTED;
-    pl->max_items = (int32_t)items;
-    const size_t fixed = 2 * (size_t)kTileKeys * rb + (size_t)kRowsPerItem * 256 * 4;
+    pl->mode = kModeStream;
+    pl->rows_per_item = kStreamWaves;
+    items = prefill_items(p, kStreamWaves);
+    const size_t fixed = 2 * tile + (size_t)kStreamWaves * kWaveScratch;
     const int k64 = (int)align_up(p->topk, 64);
-    const int fit = (int)((kLdsBudget - fixed) / (kRowsPerItem * 8) / 64 * 64);
+    const int fit = (int)((kLdsBudget - fixed) / (kStreamWaves * 8) / 64 * 64);
     int cap = std::max(2 * k64, k64 + 512);
     cap = std::min(cap, fit);
     if (cap < k64 + 64) return LI_ERR_UNSUPPORTED;
     pl->cap = cap;
-    pl->lds_prefill = fixed + (size_t)kRowsPerItem * cap * 8;
+    pl->lds_prefill = fixed + (size_t)kStreamWaves * cap * 8;
   }
+  if (items > INT32_MAX / 16) return LI_ERR_UNSUPPORTED;
+  pl->max_items = (int32_t)items;
   pl->off_batch = sizeof(MetaHeader);
   pl->off_counts = align_up(pl->off_batch + (size_t)B * 16, 16);
   pl->off_starts = align_up(pl->off_counts + (size_t)B * 4, 16);
@@ -149,8 +158,14 @@ KArgs base_args(const li_problem* p, const Plan& pl, void* metadata) {
   a.mask_mode = p->mask_mode;
   a.block_size = p->block_size;
   a.max_blocks_per_seq = p->max_blocks_per_seq;
-  a.k_block_stride = p->k_block_stride ? p->k_block_stride : (int64_t)p->block_size * kHeadDim;
+  const int64_t kbs = p->k_block_stride ? p->k_block_stride : (int64_t)p->block_size * kHeadDim;
+  a.k_block_stride_bytes = kbs * elem_bytes(p->qk_dtype);
+  a.block_shift = -1;
+  if (p->block_size > 0 && (p->block_size & (p->block_size - 1)) == 0)
+    a.block_shift = __builtin_ctz((unsigned)p->block_size);
   a.cap = pl.cap;
+  a.dcap = pl.dcap;
+  a.rows_per_item = pl.rows_per_item;
   a.chunk = pl.chunk;
   a.max_items = pl.max_items;
   a.ws_row_stride = pl.ws_row_stride;
@@ -233,15 +248,16 @@ li_status li_forward(const li_problem* p, const void* q, const void* k, const vo
   a.cu_q = cu_seqlens_q;
   a.cu_k = cu_seqlens_k;
   a.seqused_k = seqused_k;
-  a.ws = static_cast<uint32_t*>(workspace);
+  a.ws = static_cast<float*>(workspace);
   a.out_idx = sparse_indices;
   a.out_val = sparse_values;
   const int qk = p->qk_dtype, wt = p->w_dtype;
+  const bool paged = p->layout_k == LI_LAYOUT_PA_BSND;
   hipError_t e;
-  if (pl.mode == kModePrefill) {
-    e = launch_prefill(a, qk, wt, pl.mblocks, pl.max_items, pl.lds_prefill, stream);
+  if (pl.mode != kModeDecode) {
+    e = launch_prefill(a, pl.mode, qk, wt, pl.mblocks, paged, pl.max_items, pl.lds_prefill, stream);
   } else {
-    e = launch_decode(a, qk, wt, pl.mblocks, pl.max_items, stream);
+    e = launch_decode(a, qk, wt, pl.mblocks, paged, pl.max_items, stream);
     if (e == hipSuccess)
       e = launch_select(a, p->batch * p->max_seqlen_q, pl.lds_select, stream);
   }

@@ -12,15 +12,20 @@ namespace li {
 constexpr int kHeadDim = 128;
 constexpr int kMaxHeads = 64;
 constexpr int kMaxTopk = 2048;
-constexpr int kRowsPerItem = 4;        // prefill: one query row per wave, 4 waves
-constexpr int kTileKeys = 64;          // keys per score tile (two 32-key MFMA column blocks)
-constexpr int kDecodeMaxRows = 4;      // decode mode: at most this many query rows per batch
-constexpr int kSelectThreads = 1024;   // decode-mode select kernel
-constexpr int kSelectCacheKeys = 32768;// decode-mode select: rows up to this length sit in LDS
+constexpr int kTileKeys = 64;           // keys per score tile (two 32-key MFMA column blocks)
+constexpr int kDenseWaves = 8;          // dense prefill: 8 query rows per workgroup (2 waves / SIMD)
+constexpr int kStreamWaves = 4;         // streaming prefill: 4 query rows per workgroup
+constexpr int kDecodeMaxRows = 4;       // decode mode: at most this many query rows per batch
+constexpr int kDecodeWaves = 4;         // decode split kernel: waves per workgroup
+constexpr int kDecodeSegments = 2048;   // decode: target number of key segments
+constexpr int kSelectThreads = 1024;    // decode-mode select kernel
+constexpr int kSelectCacheKeys = 32768; // decode-mode select: rows up to this length sit in LDS
+constexpr int kSelectBuckets = 2048;    // decode-mode select: histogram buckets
 constexpr size_t kLdsBudget = 160 * 1024;
-constexpr int kMetaMagic = 0x4C494D44; // "LIMD"
+constexpr int kWaveScratch = 256 * 4 + 2 * 64 * 4;   // per-wave select scratch: histogram + gather
+constexpr int kMetaMagic = 0x4C494D44;  // "LIMD"
 
-enum Mode : int32_t { kModePrefill = 0, kModeDecode = 1 };
+enum Mode : int32_t { kModeDense = 0, kModeStream = 1, kModeDecode = 2 };
 
 // Metadata buffer layout (all int32 / int4 records, offsets in bytes):
 //   [0, 256)        header, see MetaHeader
@@ -44,15 +49,17 @@ static_assert(sizeof(MetaHeader) == 256, "metadata header is 256 bytes");
 struct Plan {
   int32_t mode;
   int32_t max_items;
-  int32_t chunk;          // decode: keys per item
-  int32_t cap;            // prefill: candidate slots per row
+  int32_t rows_per_item;  // prefill: query rows per work item
+  int32_t chunk;          // decode: minimum keys per segment
+  int32_t cap;            // streaming prefill: candidate slots per row
+  int32_t dcap;           // dense prefill: score slots per row
   int32_t mblocks;        // 1 (N1 <= 32) or 2 (N1 <= 64)
   size_t lds_prefill;     // dynamic LDS of the prefill kernel
   size_t lds_select;      // dynamic LDS of the decode-mode select kernel
   size_t meta_bytes;
   size_t off_batch, off_counts, off_starts, off_items;
   size_t ws_bytes;
-  int64_t ws_row_stride;  // decode: u32 slots per (batch, row) score row
+  int64_t ws_row_stride;  // decode: fp32 slots per (batch, row) score row
 };
 
 // Kernel argument block (passed by value).
@@ -67,16 +74,16 @@ struct KArgs {
   const int32_t* cu_k;
   const int32_t* seqused_k;
   unsigned char* meta;      // metadata base
-  uint32_t* ws;             // decode: dense score rows
+  float* ws;                // decode: dense score rows
   int32_t* out_idx;
   float* out_val;
-  int64_t k_block_stride;   // elements between paged blocks
+  int64_t k_block_stride_bytes;   // bytes between paged blocks
   int64_t ws_row_stride;
   int32_t batch, s1max, s2max;
   int32_t n1, topk;
   int32_t layout_q, layout_k, mask_mode;
-  int32_t block_size, max_blocks_per_seq;
-  int32_t cap, chunk, max_items;
+  int32_t block_size, block_shift, max_blocks_per_seq;
+  int32_t cap, dcap, chunk, max_items, rows_per_item;
   int32_t off_batch, off_counts, off_starts, off_items;
 };
 
@@ -86,10 +93,11 @@ enum { DT_BF16 = 0, DT_FP8 = 1, DT_FP32 = 2, DT_FP16 = 3 };
 
 // Launchers (defined in the .hip files); return the hipGetLastError() of the launch.
 hipError_t launch_metadata(const KArgs& a, int mode, hipStream_t s);
-hipError_t launch_prefill(const KArgs& a, int qk_dtype, int w_dtype, int mblocks, int grid,
-                          size_t lds, hipStream_t s);
-hipError_t launch_decode(const KArgs& a, int qk_dtype, int w_dtype, int mblocks, int grid,
-                         hipStream_t s);
+hipError_t launch_prefill(const KArgs& a, int mode, int qk_dtype, int w_dtype, int mblocks,
+                          bool paged, int grid, size_t lds, hipStream_t s);
+hipError_t launch_decode(const KArgs& a, int qk_dtype, int w_dtype, int mblocks, bool paged,
+                         int grid, hipStream_t s);
 hipError_t launch_select(const KArgs& a, int grid, size_t lds, hipStream_t s);
+size_t select_shared_bytes();   // fixed LDS of the select kernel (before the row cache)
 
 }  // namespace li

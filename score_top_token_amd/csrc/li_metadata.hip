@@ -4,11 +4,12 @@
 // (inclusive cu_seqlens for TND, seqused_k for the paged layout, the fixed BSND
 // dimensions otherwise) and writes
 //   - a batch table {q token offset, S1_b, k token offset, S2_b},
-//   - prefill mode: one item per block of 4 query rows, ordered so that the
-//     costliest blocks (the last rows of each sequence under right-down causal
-//     masking) are dispatched first, round-robin over the batches;
-//   - decode mode: one item per (batch, query row, chunk of `chunk` keys).
-// The result depends only on the lengths (deterministic) and lives on the
+//   - prefill modes: one item per block of `rows_per_item` query rows, ordered so
+//     that the costliest blocks (the last rows of each sequence under right-down
+//     causal masking) are dispatched first, round-robin over the batches;
+//   - decode mode: the visible keys of every query row cut into segments of equal
+//     length (about kDecodeSegments segments in total), one item per segment.
+// The result depends only on the lengths (deterministic) and is produced on the
 // device, so the call never synchronises with the host.
 #include "li_common_kernels.h"
 
@@ -24,8 +25,9 @@ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mode) {
   __shared__ int s_counts[kRoundRobinMaxBatch];
   __shared__ int s_part[kMetaThreads / 64];
-  __shared__ int s_total;
-  const int tid = threadIdx.x;
+  __shared__ long long s_vis[kMetaThreads / 64];
+  __shared__ int s_total, s_chunk;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int B = a.batch;
   MetaHeader* hdr = reinterpret_cast<MetaHeader*>(a.meta);
   int4* bt = reinterpret_cast<int4*>(a.meta + a.off_batch);
@@ -33,7 +35,8 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
   int* starts = reinterpret_cast<int*>(a.meta + a.off_starts);
   int4* items = reinterpret_cast<int4*>(a.meta + a.off_items);
 
-  // 1. per-batch lengths and item counts
+  // 1. per-batch lengths (and, for decode, the visible keys of its rows)
+  long long vis = 0;
   for (int b = tid; b < B; b += kMetaThreads) {
     int q_off, s1, k_off, s2;
     if (a.layout_q == L_TND) {
@@ -54,11 +57,34 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
       s2 = a.s2max;
     }
     bt[b] = int4{q_off, s1, k_off, s2};
+    if (mode == kModeDecode)
+      for (int i = 0; i < s1; ++i) vis += visible_limit(a.mask_mode, i, s1, s2);
+  }
+  // decode segment length from the total number of visible keys
+  if (mode == kModeDecode) {
+    for (int o = 32; o > 0; o >>= 1) vis += __shfl_xor(vis, o);
+    if (lane == 0) s_vis[wave] = vis;
+    __syncthreads();
+    if (tid == 0) {
+      long long tot = 0;
+      for (int w = 0; w < kMetaThreads / 64; ++w) tot += s_vis[w];
+      long long c = (tot + kDecodeSegments - 1) / kDecodeSegments;
+      c = (c + kTileKeys - 1) / kTileKeys * kTileKeys;
+      s_chunk = (int)(c > a.chunk ? c : a.chunk);
+    }
+  } else if (tid == 0) {
+    s_chunk = a.chunk;
+  }
+  __syncthreads();
+  const int chunk = s_chunk;
+
+  for (int b = tid; b < B; b += kMetaThreads) {
+    const int4 rec = bt[b];
     int cnt = 0;
-    if (mode == kModePrefill) {
-      cnt = cdiv(s1, kRowsPerItem);
+    if (mode == kModeDecode) {
+      for (int i = 0; i < rec.y; ++i) cnt += cdiv(visible_limit(a.mask_mode, i, rec.y, rec.w), chunk);
     } else {
-      for (int i = 0; i < s1; ++i) cnt += cdiv(visible_limit(a.mask_mode, i, s1, s2), a.chunk);
+      cnt = cdiv(rec.y, a.rows_per_item);
     }
     counts[b] = cnt;
     if (B <= kRoundRobinMaxBatch) s_counts[b] = cnt;
@@ -70,7 +96,6 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
   const int b0 = tid * seg, b1 = min(b0 + seg, B);
   int local = 0;
   for (int b = b0; b < b1; ++b) local += counts[b];
-  const int wave = tid >> 6, lane = tid & 63;
   const int incl = wave_prefix_sum(local);
   if (lane == 63) s_part[wave] = incl;
   __syncthreads();
@@ -93,7 +118,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
   if (tid == 0) {
     hdr->n_items = total;
     hdr->mode = mode;
-    hdr->chunk = a.chunk;
+    hdr->chunk = chunk;
     hdr->magic = kMetaMagic;
     hdr->batch = B;
     hdr->max_items = a.max_items;
@@ -111,11 +136,11 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
     const int b = lo;
     const int r = u - starts[b];
     const int4 rec = bt[b];
-    if (mode == kModePrefill) {
+    if (mode != kModeDecode) {
       const int cnt = counts[b];
       const int blk = cnt - 1 - r;                 // r = 0 is the last (costliest) block
-      const int q0 = blk * kRowsPerItem;
-      const int nrows = min(kRowsPerItem, rec.y - q0);
+      const int q0 = blk * a.rows_per_item;
+      const int nrows = min(a.rows_per_item, rec.y - q0);
       int pos = u;
       if (B <= kRoundRobinMaxBatch) {
         // round-robin over batches, each batch walked from its last block:
@@ -131,12 +156,12 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
       int rest = r, i = 0, lim = 0;
       for (; i < rec.y; ++i) {
         lim = visible_limit(a.mask_mode, i, rec.y, rec.w);
-        const int nch = cdiv(lim, a.chunk);
+        const int nch = cdiv(lim, chunk);
         if (rest < nch) break;
         rest -= nch;
       }
-      const int k0 = rest * a.chunk;
-      const int k1 = min(k0 + a.chunk, lim);
+      const int k0 = rest * chunk;
+      const int k1 = min(k0 + chunk, lim);
       items[u] = int4{b, i, k0, k1};
     }
   }

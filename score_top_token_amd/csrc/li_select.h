@@ -1,0 +1,241 @@
+// Exact k-th element selection for the top-k step.
+//
+// Order: value descending, then key index ascending (the smaller index wins a
+// tie).  Given the k-th element (fb, eb) of that order, key e with value f is in
+// the top k iff  f > fb  or  (f == fb and e <= eb).
+//
+// Method (bucket select, exact):
+//   1. one histogram over 256 buckets linear in value between the candidates'
+//      min and max (computed in fp32; the bucket map is monotone, so every key of
+//      a higher bucket is strictly larger than every key of a lower bucket);
+//   2. the bucket holding the k-th element is found from the suffix counts;
+//   3. if it holds few candidates (<= 64) they are gathered and ranked exactly;
+//      otherwise the search continues on that bucket with buckets of the
+//      order-preserving u32 keys, each pass cutting the key range by 256, until
+//      few candidates remain or all remaining candidates are equal, in which case
+//      the tie rule alone decides (the r-th of them in index order).
+// Values are never NaN; -0 has been folded into +0 by the producer.
+#pragma once
+
+#include "li_device.h"
+
+namespace li {
+
+constexpr int kSelSmall = 64;
+
+__device__ inline float wave_min_f(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ inline float wave_max_f(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ inline uint32_t wave_min_u(uint32_t v) {
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+__device__ inline uint32_t wave_max_u(uint32_t v) {
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+
+// Linear value bucket in [0, 255]; halving first keeps (hi - lo) finite.
+struct FBucket {
+  float lo2, scale;
+  __device__ FBucket(float lo, float hi) {
+    lo2 = lo * 0.5f;
+    const float d = hi * 0.5f - lo2;
+    scale = fminf(256.0f / d, 3.0e38f);
+  }
+  __device__ uint32_t operator()(float f) const {
+    const float x = fminf((f * 0.5f - lo2) * scale, 255.0f);
+    return (uint32_t)fmaxf(x, 0.0f);
+  }
+};
+
+// Bucket of u32 keys in [ulo, uhi]: (u - ulo) >> shift, at most 255.
+struct UBucket {
+  uint32_t ulo;
+  int shift;
+  __device__ UBucket(uint32_t lo, uint32_t hi) : ulo(lo) {
+    const uint32_t span = hi - lo;
+    const int bits = span ? 32 - __clz(span) : 0;
+    shift = bits > 8 ? bits - 8 : 0;
+  }
+  __device__ uint32_t operator()(uint32_t u) const {
+    const uint32_t b = (u - ulo) >> shift;
+    return b > 255u ? 255u : b;
+  }
+};
+
+// Finds, from 256 bucket counts (lane l owns buckets 4l..4l+3), the bucket that
+// holds the element of rank r (1-based) counted from the top.  Returns the
+// bucket, the number of candidates in higher buckets and in the bucket itself.
+__device__ inline void wave_find_bucket(const uint32_t* hist, int r, int& bkt, int& above, int& cnt) {
+  const int l = lane_id();
+  const uint32_t h0 = hist[4 * l], h1 = hist[4 * l + 1], h2 = hist[4 * l + 2], h3 = hist[4 * l + 3];
+  const int s = (int)(h0 + h1 + h2 + h3);
+  const int suf = wave_suffix_sum(s);
+  const int ab = suf - s;
+  const bool mine = ab < r && r <= suf;
+  int b = 0, a = 0, c = 0;
+  if (mine) {
+    if (ab + (int)h3 >= r) { b = 4 * l + 3; a = ab; c = h3; }
+    else if (ab + (int)(h3 + h2) >= r) { b = 4 * l + 2; a = ab + h3; c = h2; }
+    else if (ab + (int)(h3 + h2 + h1) >= r) { b = 4 * l + 1; a = ab + h3 + h2; c = h1; }
+    else { b = 4 * l; a = ab + h3 + h2 + h1; c = h0; }
+  }
+  const uint64_t who = ballot(mine);
+  const int src = who ? (int)__builtin_ctzll(who) : 0;
+  bkt = __shfl(b, src);
+  above = __shfl(a, src);
+  cnt = __shfl(c, src);
+}
+
+// Exact rank of the (<= 64) gathered candidates, one per lane (lanes >= m idle):
+// returns the element of rank r (1-based) in (value desc, index asc) order.
+__device__ inline void wave_rank_small(float f, uint32_t e, int m, int r, float& fb, uint32_t& eb) {
+  const int l = lane_id();
+  int rank = 0;
+  for (int j = 0; j < m; ++j) {
+    const float fj = __shfl(f, j);
+    const uint32_t ej = (uint32_t)__shfl((int)e, j);
+    rank += (fj > f || (fj == f && ej < e)) ? 1 : 0;
+  }
+  const bool hit = l < m && rank == r - 1;
+  const uint64_t who = ballot(hit);
+  const int src = who ? (int)__builtin_ctzll(who) : 0;
+  fb = __shfl(f, src);
+  eb = (uint32_t)__shfl((int)e, src);
+}
+
+// Gathers the (<= kSelSmall) candidates selected by `in(p)` into lane order via
+// the wave's LDS scratch (kSelSmall floats + kSelSmall u32), ascending position.
+template <class Pred>
+__device__ inline int wave_gather(const float* vals, const uint32_t* idx, int n, float* sf,
+                                  uint32_t* se, Pred in, float& cf, uint32_t& ce) {
+  const int l = lane_id();
+  int got = 0;
+  for (int p0 = 0; p0 < n; p0 += 64) {
+    const int p = p0 + l;
+    const float f = p < n ? vals[p] : 0.0f;
+    const bool take = p < n && in(f);
+    const uint64_t m = ballot(take);
+    if (take) {
+      const int slot = got + mbcnt(m);
+      if (slot < kSelSmall) {
+        sf[slot] = f;
+        se[slot] = idx ? idx[p] : (uint32_t)p;
+      }
+    }
+    got += __popcll(m);
+  }
+  wave_sync();
+  cf = l < got ? sf[l] : 0.0f;
+  ce = l < got ? se[l] : 0u;
+  wave_sync();
+  return got;
+}
+
+// Wave-level k-th element of vals[0, n) (LDS).  idx == nullptr: the index of
+// entry p is p (a dense score row); otherwise idx[p] (the list is in ascending
+// index order).  lo / hi: bounds of the n values (min and max for speed).
+// hist: 256 u32 and scr: 2 * kSelSmall words of LDS private to the wave.
+// 1 <= k <= n.
+__device__ inline void wave_kth(const float* vals, const uint32_t* idx, int n, int k, float lo,
+                                float hi, uint32_t* hist, uint32_t* scr, float& fb, uint32_t& eb) {
+  const int l = lane_id();
+  float* sf = reinterpret_cast<float*>(scr);
+  uint32_t* se = scr + kSelSmall;
+  int r = k;
+  uint32_t ulo, uhi;
+  // ---- pass 1: linear value buckets ------------------------------------
+  if (lo < hi) {
+    const FBucket fbk(lo, hi);
+    for (int x = l; x < 256; x += 64) hist[x] = 0;
+    wave_sync();
+    for (int p = l; p < n; p += 64) atomicAdd(&hist[fbk(vals[p])], 1u);
+    wave_sync();
+    int B, above, cnt;
+    wave_find_bucket(hist, r, B, above, cnt);
+    r -= above;
+    wave_sync();
+    const uint32_t ub = (uint32_t)B;
+    if (cnt <= kSelSmall) {
+      float cf;
+      uint32_t ce;
+      const int got = wave_gather(vals, idx, n, sf, se, [&](float f) { return fbk(f) == ub; }, cf, ce);
+      wave_rank_small(cf, ce, got, r, fb, eb);
+      return;
+    }
+    // key range of the chosen bucket, then continue on u32 keys
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int p = l; p < n; p += 64) {
+      const float f = vals[p];
+      if (fbk(f) == ub) {
+        const uint32_t u = f2key(f);
+        mn = min(mn, u);
+        mx = max(mx, u);
+      }
+    }
+    ulo = wave_min_u(mn);
+    uhi = wave_max_u(mx);
+  } else {
+    ulo = uhi = f2key(lo);
+  }
+  // ---- exact passes on u32 keys ------------------------------------------
+  for (;;) {
+    if (ulo == uhi) {
+      // every remaining candidate equals this key: the r-th of them in index order
+      fb = key2f(ulo);
+      eb = 0;
+      int seen = 0;
+      for (int p0 = 0; p0 < n; p0 += 64) {
+        const int p = p0 + l;
+        const bool eq = p < n && f2key(vals[p]) == ulo;
+        const uint64_t m = ballot(eq);
+        const int c = __popcll(m);
+        if (seen + c >= r) {
+          const bool hit = eq && seen + mbcnt(m) == r - 1;
+          const uint64_t who = ballot(hit);
+          const int src = who ? (int)__builtin_ctzll(who) : 0;
+          const uint32_t e = idx ? (p < n ? idx[p] : 0u) : (uint32_t)p;
+          eb = (uint32_t)__shfl((int)e, src);
+          return;
+        }
+        seen += c;
+      }
+      return;
+    }
+    const UBucket ubk(ulo, uhi);
+    for (int x = l; x < 256; x += 64) hist[x] = 0;
+    wave_sync();
+    for (int p = l; p < n; p += 64) {
+      const uint32_t u = f2key(vals[p]);
+      if (u >= ulo && u <= uhi) atomicAdd(&hist[ubk(u)], 1u);
+    }
+    wave_sync();
+    int B, above, cnt;
+    wave_find_bucket(hist, r, B, above, cnt);
+    r -= above;
+    wave_sync();
+    const uint32_t nlo = ulo + ((uint32_t)B << ubk.shift);
+    uint32_t nhi = (B == 255) ? uhi : nlo + ((1u << ubk.shift) - 1u);
+    if (nhi > uhi) nhi = uhi;
+    if (cnt <= kSelSmall && nlo != nhi) {
+      float cf;
+      uint32_t ce;
+      const int got = wave_gather(vals, idx, n, sf, se, [&](float f) {
+        const uint32_t u = f2key(f);
+        return u >= nlo && u <= nhi;
+      }, cf, ce);
+      wave_rank_small(cf, ce, got, r, fb, eb);
+      return;
+    }
+    ulo = nlo;
+    uhi = nhi;
+  }
+}
+
+}  // namespace li
