@@ -87,13 +87,61 @@ __device__ inline void load_query(const KArgs& a, int64_t tok, int lane,
                               : zero_frag<QK>();
   }
   const float qd = (QK == DT_FP8) ? a.q_descale[tok] : 1.0f;
+  // accumulator rows 4g .. 4g+3 of a lane are 4 consecutive heads
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int h0 = mb * 32 + acc_row(lane, 4 * g);
+      if (h0 + 3 < a.n1 && ((tok * a.n1 + h0) & 3) == 0) {
+        if constexpr (WT == DT_FP32) {
+          const float4 v = *reinterpret_cast<const float4*>(
+              reinterpret_cast<const float*>(a.w) + tok * a.n1 + h0);
+          wv[mb][4 * g] = v.x * qd;
+          wv[mb][4 * g + 1] = v.y * qd;
+          wv[mb][4 * g + 2] = v.z * qd;
+          wv[mb][4 * g + 3] = v.w * qd;
+        } else {
+          const uint2 v = *reinterpret_cast<const uint2*>(
+              reinterpret_cast<const uint16_t*>(a.w) + tok * a.n1 + h0);
+          wv[mb][4 * g] = __uint_as_float(v.x << 16) * qd;
+          wv[mb][4 * g + 1] = __uint_as_float(v.x & 0xFFFF0000u) * qd;
+          wv[mb][4 * g + 2] = __uint_as_float(v.y << 16) * qd;
+          wv[mb][4 * g + 3] = __uint_as_float(v.y & 0xFFFF0000u) * qd;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          wv[mb][4 * g + q] = h0 + q < a.n1 ? load_w<WT>(a.w, tok * a.n1 + h0 + q) * qd : 0.0f;
+      }
+    }
+}
+
+// max(x, 0) on the bit pattern: a negative float is a negative int32, so the
+// integer max yields +0; one VALU op with no NaN canonicalisation.
+__device__ inline float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// ReLU, per-head weight and head sum of the two 32-key column blocks of a
+// 64-key tile, acc[mb][nb].  Lanes 0-31 hold half of the heads of keys 0-31
+// (block 0) and 32-63 (block 1), lanes 32-63 the other half; after the
+// exchange lane l holds the full score of key l of the tile.  Four independent
+// chains per block keep the FMA latency off the critical path.
+template <int MB>
+__device__ inline float head_sum(const f32x16 (&acc)[MB][2], const float (&wv)[MB][16], int lane) {
+  float p0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, p1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int h = mb * 32 + acc_row(lane, r);
-      wv[mb][r] = h < a.n1 ? load_w<WT>(a.w, tok * a.n1 + h) * qd : 0.0f;
+      p0[r & 3] = fmaf(wv[mb][r], relu(acc[mb][0][r]), p0[r & 3]);
+      p1[r & 3] = fmaf(wv[mb][r], relu(acc[mb][1][r]), p1[r & 3]);
     }
+  const float s0 = (p0[0] + p0[1]) + (p0[2] + p0[3]);
+  const float s1 = (p1[0] + p1[1]) + (p1[2] + p1[3]);
+  const bool lo = lane < 32;
+  const float send = lo ? s1 : s0;
+  const float recv = __shfl_xor(send, 32);
+  return (lo ? s0 : s1) + recv;
 }
 
 template <int QK, int MB>
@@ -134,20 +182,7 @@ __device__ inline float score_tile_lds(const unsigned char* tile,
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = M::mma(qf[mb][j], kb[nb][j], acc[mb][nb]);
-  // ReLU, per-head weight and head sum; lanes 0-31 hold half of the heads of
-  // keys 0-31 (block 0) and 32-63 (block 1), lanes 32-63 the other half.
-  float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p0 = fmaf(wv[mb][r], fmaxf(acc[mb][0][r], 0.0f), p0);
-      p1 = fmaf(wv[mb][r], fmaxf(acc[mb][1][r], 0.0f), p1);
-    }
-  const bool lo = lane < 32;
-  const float send = lo ? p1 : p0;
-  const float recv = __shfl_xor(send, 32);
-  return (lo ? p0 : p1) + recv;
+  return head_sum<MB>(acc, wv, lane);
 }
 
 // Cooperative staging of one 64-key K tile: NT threads load it from global

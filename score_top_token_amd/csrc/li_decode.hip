@@ -64,31 +64,22 @@ __device__ inline float score_tile_regs(const typename Mma<QK>::frag (&qf)[MB][M
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = M::mma(qf[mb][j], kf[nb][j], acc[mb][nb]);
-  float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p0 = fmaf(wv[mb][r], fmaxf(acc[mb][0][r], 0.0f), p0);
-      p1 = fmaf(wv[mb][r], fmaxf(acc[mb][1][r], 0.0f), p1);
-    }
-  const bool lo = lane < 32;
-  const float send = lo ? p1 : p0;
-  const float recv = __shfl_xor(send, 32);
-  return (lo ? p0 : p1) + recv;
+  return head_sum<MB>(acc, wv, lane);
 }
 
+// One wave per segment (item): waves of a workgroup work independently.
 template <int QK, int MB, int WT, bool PAGED>
 __global__ __launch_bounds__(kDecodeWaves * 64, 1) void split_kernel(KArgs a) {
   typedef Mma<QK> M;
   typedef typename M::frag F;
-  constexpr int STEP = kDecodeWaves * kTileKeys;
+  constexpr int STEP = kTileKeys;
   const MetaHeader* hdr = reinterpret_cast<const MetaHeader*>(a.meta);
-  if ((int)blockIdx.x >= hdr->n_items) return;
-  const int4 item = reinterpret_cast<const int4*>(a.meta + a.off_items)[blockIdx.x];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int it = blockIdx.x * kDecodeWaves + wave;
+  if (it >= hdr->n_items) return;
+  const int4 item = reinterpret_cast<const int4*>(a.meta + a.off_items)[it];
   const int b = item.x, i = item.y, k0 = item.z, k1 = item.w;
   const int4 br = batch_rec(a, b);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t tok = (int64_t)br.x + i;
 
   F qf[MB][M::KSTEPS];
@@ -100,13 +91,14 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void split_kernel(KArgs a) {
     const int s = base + lane;
     if (s < k1) {
       if constexpr (QK == DT_FP8) tot *= a.k_descale[slot];
-      dst[s] = tot == 0.0f ? 0.0f : tot;
+      // -0 -> +0; NaN (only from NaN inputs) -> -inf keeps the scores ordered
+      dst[s] = tot == 0.0f ? 0.0f : (tot != tot ? -__builtin_inff() : tot);
     }
   };
 
   F ka[2][M::KSTEPS], kb[2][M::KSTEPS];
   int64_t sa = 0, sb = 0;
-  int base = k0 + wave * kTileKeys;
+  int base = k0;
   if (base < k1) load_key_frags<QK, PAGED>(a, b, br.z, base, k1, lane, ka, sa);
   while (base < k1) {
     if (base + STEP < k1) load_key_frags<QK, PAGED>(a, b, br.z, base + STEP, k1, lane, kb, sb);
@@ -440,8 +432,10 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(KArgs a) {
     const uint64_t m = ballot(keep);
     if (keep) {
       const int o = pos + mbcnt(m);
-      oi[o] = p;
-      if (ov) ov[o] = f;
+      if (o < topk) {                      // bounded whatever the data
+        oi[o] = p;
+        if (ov) ov[o] = f;
+      }
     }
     pos += __popcll(m);
   }

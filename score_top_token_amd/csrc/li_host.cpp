@@ -5,7 +5,7 @@
 
 #include <algorithm>
 
-#include "../../include/li.h"
+#include "li.h"
 #include "li_internal.h"
 
 using namespace li;
@@ -95,8 +95,9 @@ li_status make_plan(const li_problem* p, Plan* pl) {
   int64_t items;
   if (use_decode(p)) {
     pl->mode = kModeDecode;
-    pl->chunk = 256;                      // minimum segment; the device picks the real one
-    items = (int64_t)B * p->max_seqlen_q + kDecodeSegments;
+    pl->chunk = kTileKeys;                // minimum segment; the device picks the real one
+    // segments <= target + rows, target <= kDecodeSegments + 2 * rows
+    items = 3 * (int64_t)B * p->max_seqlen_q + kDecodeSegments;
     pl->ws_row_stride = (int64_t)align_up(p->max_seqlen_k, 64);
     pl->ws_bytes = (size_t)B * p->max_seqlen_q * pl->ws_row_stride * 4;
     const int cache = std::min(p->max_seqlen_k, kSelectCacheKeys);
@@ -257,7 +258,8 @@ li_status li_forward(const li_problem* p, const void* q, const void* k, const vo
   if (pl.mode != kModeDecode) {
     e = launch_prefill(a, pl.mode, qk, wt, pl.mblocks, paged, pl.max_items, pl.lds_prefill, stream);
   } else {
-    e = launch_decode(a, qk, wt, pl.mblocks, paged, pl.max_items, stream);
+    e = launch_decode(a, qk, wt, pl.mblocks, paged,
+                      (int)cdiv64(pl.max_items, kDecodeWaves), stream);
     if (e == hipSuccess)
       e = launch_select(a, p->batch * p->max_seqlen_q, pl.lds_select, stream);
   }

@@ -13,11 +13,11 @@ constexpr int kHeadDim = 128;
 constexpr int kMaxHeads = 64;
 constexpr int kMaxTopk = 2048;
 constexpr int kTileKeys = 64;           // keys per score tile (two 32-key MFMA column blocks)
-constexpr int kDenseWaves = 8;          // dense prefill: 8 query rows per workgroup (2 waves / SIMD)
+constexpr int kDenseWaves = 4;          // dense prefill: 4 query rows per workgroup, 2 workgroups / CU
 constexpr int kStreamWaves = 4;         // streaming prefill: 4 query rows per workgroup
 constexpr int kDecodeMaxRows = 4;       // decode mode: at most this many query rows per batch
 constexpr int kDecodeWaves = 4;         // decode split kernel: waves per workgroup
-constexpr int kDecodeSegments = 2048;   // decode: target number of key segments
+constexpr int kDecodeSegments = 1024;   // decode: key segments per pass (256 CUs x 4 waves)
 constexpr int kSelectThreads = 1024;    // decode-mode select kernel
 constexpr int kSelectCacheKeys = 32768; // decode-mode select: rows up to this length sit in LDS
 constexpr int kSelectBuckets = 2048;    // decode-mode select: histogram buckets

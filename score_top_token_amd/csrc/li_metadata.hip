@@ -26,6 +26,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
   __shared__ int s_counts[kRoundRobinMaxBatch];
   __shared__ int s_part[kMetaThreads / 64];
   __shared__ long long s_vis[kMetaThreads / 64];
+  __shared__ long long s_rows[kMetaThreads / 64];
   __shared__ int s_total, s_chunk;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int B = a.batch;
@@ -60,15 +61,30 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
     if (mode == kModeDecode)
       for (int i = 0; i < s1; ++i) vis += visible_limit(a.mask_mode, i, s1, s2);
   }
-  // decode segment length from the total number of visible keys
+  // decode segment length from the total number of visible keys: one segment per
+  // wave of a full GPU (kDecodeSegments, more if there are many rows); every row
+  // adds at most one partial segment, so the count stays within the target.
   if (mode == kModeDecode) {
-    for (int o = 32; o > 0; o >>= 1) vis += __shfl_xor(vis, o);
-    if (lane == 0) s_vis[wave] = vis;
+    long long rows = 0;
+    for (int b = tid; b < B; b += kMetaThreads) rows += bt[b].y;
+    for (int o = 32; o > 0; o >>= 1) {
+      vis += __shfl_xor(vis, o);
+      rows += __shfl_xor(rows, o);
+    }
+    if (lane == 0) {
+      s_vis[wave] = vis;
+      s_rows[wave] = rows;
+    }
     __syncthreads();
     if (tid == 0) {
-      long long tot = 0;
-      for (int w = 0; w < kMetaThreads / 64; ++w) tot += s_vis[w];
-      long long c = (tot + kDecodeSegments - 1) / kDecodeSegments;
+      long long tot = 0, nrows = 0;
+      for (int w = 0; w < kMetaThreads / 64; ++w) {
+        tot += s_vis[w];
+        nrows += s_rows[w];
+      }
+      long long target = kDecodeSegments;
+      while (target < 2 * nrows) target += kDecodeSegments;
+      long long c = (tot + (target - nrows) - 1) / (target - nrows);
       c = (c + kTileKeys - 1) / kTileKeys * kTileKeys;
       s_chunk = (int)(c > a.chunk ? c : a.chunk);
     }

@@ -1,0 +1,126 @@
+// Software-pipelined score loop shared by the prefill kernels.
+//
+// The K stream is cut into 32-key tiles (one MFMA column block), double-buffered
+// in LDS.  In iteration t a wave reads tile t's fragments, issues its MFMAs into
+// one accumulator set and, interleaved with them, runs the ReLU / weight / head
+// sum of tile t-1 from the other set, so the matrix cores and the vector ALUs
+// work at the same time.  One barrier per tile: the store of tile t+1 into the
+// other buffer and the loads of tile t+2 into registers overlap the compute.
+#pragma once
+
+#include "li_common_kernels.h"
+
+namespace li {
+
+constexpr int kPipeKeys = 32;
+
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
+// fragments of one 32-key tile
+template <int QK>
+__device__ inline void read_tile_frags(const unsigned char* tile, int lane,
+                                       typename Mma<QK>::frag (&kb)[Mma<QK>::KSTEPS]) {
+#pragma unroll
+  for (int j = 0; j < Mma<QK>::KSTEPS; ++j) kb[j] = load_frag_lds<QK>(tile, lane & 31, lane, j);
+}
+
+template <int QK, int MB>
+__device__ inline void mma_tile(const typename Mma<QK>::frag (&qf)[MB][Mma<QK>::KSTEPS],
+                                const typename Mma<QK>::frag (&kb)[Mma<QK>::KSTEPS],
+                                f32x16 (&acc)[MB]) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
+#pragma unroll
+  for (int j = 0; j < Mma<QK>::KSTEPS; ++j)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = Mma<QK>::mma(qf[mb][j], kb[j], acc[mb]);
+}
+
+// ReLU / weight / head sum of one 32-key block; lane l (and l + 32) ends with
+// the score of key l % 32.
+template <int MB>
+__device__ inline float block_score(const f32x16 (&acc)[MB], const float (&wv)[MB][16]) {
+  float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r & 3] = fmaf(wv[mb][r], relu(acc[mb][r]), p[r & 3]);
+  const float s = (p[0] + p[1]) + (p[2] + p[3]);
+  return s + __shfl_xor(s, 32);
+}
+
+// Interleave hint for one pipelined iteration: each MFMA is followed by a few
+// VALU instructions of the previous tile's epilogue.
+template <int QK, int MB>
+__device__ inline void pipe_schedule() {
+  constexpr int NMFMA = MB * Mma<QK>::KSTEPS;
+  constexpr int NVALU = MB * 32 + 8;
+  constexpr int PER = (NVALU + NMFMA - 1) / NMFMA;
+  constexpr int NREAD = Mma<QK>::KSTEPS * Mma<QK>::FB / 16;
+  // fragment reads of the first half of the k-steps, their MFMAs (each followed
+  // by VALU work), then the second half: half the fragment registers suffice
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    __builtin_amdgcn_sched_group_barrier(0x100, NREAD / 2, 0);
+#pragma unroll
+    for (int i = 0; i < NMFMA / 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, PER, 0); // then VALU work
+    }
+  }
+}
+
+// Staging of 32-key K tiles by NT threads (global -> registers -> LDS) through
+// a ring of D register sets, so a tile's loads are issued D steps before it is
+// stored into LDS and the L2 latency hides behind D steps of compute.  Tiles at
+// or past kend are not loaded; in the tile that crosses kend the rows past it
+// are re-read from row kend-1 (their scores are masked, their content is
+// irrelevant).  Contiguous keys use one uniform tile address plus a constant
+// 32-bit lane offset.  Set indices are compile-time constants so the ring
+// stays in registers.
+template <int QK, bool PAGED, int NT, int D>
+struct PipeStage {
+  static constexpr int RB = Mma<QK>::RB;
+  static constexpr int NCH = RB / 16;
+  static constexpr int CHUNKS = kPipeKeys * NCH;
+  static constexpr int LOADS = (CHUNKS + NT - 1) / NT;
+  static_assert(CHUNKS % NT == 0, "a tile is an exact number of chunks per thread");
+  i32x4 pre[D][LOADS];
+
+  template <int S>
+  __device__ inline void load(const KArgs& a, int b, int k_off, int base, int kend, int tid) {
+    if (base >= kend) return;                        // uniform: past the visible keys
+    const int last = kend - 1 - base;                // last valid key of this tile
+    const bool full = last >= kPipeKeys - 1;         // uniform
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+      const int id = tid + NT * r;
+      int key = id / NCH;
+      const int c = id % NCH;
+      if (!full) key = key < last ? key : last;
+      if constexpr (PAGED) {
+        pre[S][r] = *reinterpret_cast<const i32x4*>(key_row<QK, true>(a, b, k_off, base + key) + c * 16);
+      } else {
+        const unsigned char* tile = reinterpret_cast<const unsigned char*>(a.k) +
+                                    ((int64_t)k_off + base) * RB;
+        pre[S][r] = *reinterpret_cast<const i32x4*>(tile + (uint32_t)(key * RB + c * 16));
+      }
+    }
+  }
+  template <int S>
+  __device__ inline void store(unsigned char* tile, int tid) const {
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+      const int id = tid + NT * r;
+      const int key = id / NCH, c = id % NCH;
+      *reinterpret_cast<i32x4*>(tile + lds_chunk_off<QK>(key, c)) = pre[S][r];
+    }
+  }
+};
+
+constexpr int kStageDepth = 2;   // 2 or 4 (4 exceeds the register budget at 64 heads)
+
+}  // namespace li

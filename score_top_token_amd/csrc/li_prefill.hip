@@ -8,28 +8,37 @@
 // owns one query row; the workgroup shares each 64-key K tile through LDS.
 //
 // Top-k (lightning_indexer page, step 3; -1 / -inf padding from its Constraints):
-//  - dense kernel (rows of at most `dcap` visible keys): 8 waves, each keeps its
+//  - dense kernel (rows of at most `dcap` visible keys): 4 waves, each keeps its
 //    row's scores in LDS, indexed by key; rows with no more visible keys than k
 //    are written straight to the output, the others pick their k-th element with
-//    the exact bucket select and write the kept keys in ascending key order;
+//    the exact bucket select and write the kept keys in ascending key order.  At
+//    <= 80 KiB of LDS two workgroups share a CU, so one workgroup's MFMAs run
+//    while the other is in its epilogue, select or output phase;
 //  - streaming kernel (longer rows): 4 waves, each keeps a list of up to `cap`
 //    (score, key) candidates in ascending key order.  A key enters when it beats
 //    the running threshold; a full list is cut back to exactly k entries by the
 //    exact select (ties to smaller keys) and the threshold rises to the k-th
 //    score.  Keys arrive in increasing order, so a later key never wins a tie.
 #include "li_common_kernels.h"
+#include "li_pipe.h"
 #include "li_select.h"
 
 namespace li {
 
 namespace {
 
-__device__ inline float canon(float f) { return f == 0.0f ? 0.0f : f; }   // -0 -> +0
+// -0 -> +0, and NaN (only possible from NaN inputs) -> -inf, so that every
+// stored score is ordered and the exact select's counting invariant holds.
+__device__ inline float canon(float f) {
+  if (f == 0.0f) return 0.0f;
+  return f != f ? -__builtin_inff() : f;
+}
 
 // Writes the top-k of a score row in ascending key order, given its k-th element.
-// vals: LDS scores; idx: LDS keys or nullptr (key = position).
+// vals: LDS scores; idx: LDS keys or nullptr (key = position).  At most topk
+// entries are written whatever the data.
 __device__ inline void write_kept(const float* vals, const uint32_t* idx, int n, float fb,
-                                  uint32_t eb, int32_t* oi, float* ov) {
+                                  uint32_t eb, int32_t* oi, float* ov, int topk) {
   const int l = lane_id();
   int kept = 0;
   for (int p0 = 0; p0 < n; p0 += 64) {
@@ -45,8 +54,10 @@ __device__ inline void write_kept(const float* vals, const uint32_t* idx, int n,
     const uint64_t m = ballot(keep);
     if (keep) {
       const int pos = kept + mbcnt(m);
-      oi[pos] = (int32_t)e;
-      if (ov) ov[pos] = f;
+      if (pos < topk) {
+        oi[pos] = (int32_t)e;
+        if (ov) ov[pos] = f;
+      }
     }
     kept += __popcll(m);
   }
@@ -60,15 +71,15 @@ __device__ inline void write_padding(int n, int topk, int32_t* oi, float* ov) {
 }
 
 // ---------------------------------------------------------------------------
-// dense kernel: 8 rows per workgroup, scores of a row kept densely in LDS
+// dense kernel: 4 rows per workgroup, scores of a row kept densely in LDS
 // ---------------------------------------------------------------------------
 template <int QK, int MB, int WT, bool PAGED>
-__global__ __launch_bounds__(kDenseWaves * 64, 1) void dense_kernel(KArgs a) {
+__global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
   typedef Mma<QK> M;
   typedef typename M::frag F;
   constexpr int NT = kDenseWaves * 64;
-  constexpr int TILE_BYTES = kTileKeys * M::RB;
-  constexpr int R0 = TILE_BYTES > kDenseWaves * kWaveScratch ? TILE_BYTES : kDenseWaves * kWaveScratch;
+  constexpr int TILE = kPipeKeys * M::RB;
+  constexpr int R0 = 2 * TILE > kDenseWaves * kWaveScratch ? 2 * TILE : kDenseWaves * kWaveScratch;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const MetaHeader* hdr = reinterpret_cast<const MetaHeader*>(a.meta);
@@ -79,14 +90,13 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void dense_kernel(KArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int topk = a.topk;
 
-  unsigned char* tile = smem;
   float* row = reinterpret_cast<float*>(smem + R0) + wave * a.dcap;
 
   const bool has_row = wave < nrows;
   const int i = q0 + wave;
   const int lim = has_row ? visible_limit(a.mask_mode, i, br.y, br.w) : 0;
   const int kend = visible_limit(a.mask_mode, q0 + nrows - 1, br.y, br.w);
-  const int ntiles = (kend + kTileKeys - 1) / kTileKeys;
+  const int ntiles = (kend + kPipeKeys - 1) / kPipeKeys;
   const int64_t tok = (int64_t)br.x + i;
   const bool direct = lim <= topk;
   int32_t* oi = a.out_idx + tok * topk;
@@ -97,34 +107,63 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void dense_kernel(KArgs a) {
   if (has_row) load_query<QK, MB, WT>(a, tok, lane, qf, wv);
   else zero_query<QK, MB>(qf, wv);
 
-  float vmin = __builtin_inff(), vmax = -__builtin_inff();
-  TileStage<QK, PAGED, NT> st;
-  if (ntiles > 0) st.load(a, b, br.z, 0, kend, tid);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();                       // every wave is done with the previous tile
-    st.store(tile, tid);
-    __syncthreads();                       // tile t is in LDS
-    if (t + 1 < ntiles) st.load(a, b, br.z, (t + 1) * kTileKeys, kend, tid);
-    const int base = t * kTileKeys;
-    if (base < lim) {
-      float tot = score_tile_lds<QK, MB>(tile, qf, wv, lane);
-      const int s = base + lane;
-      const bool valid = s < lim;
-      if constexpr (QK == DT_FP8) {
-        if (valid) tot *= a.k_descale[key_slot<PAGED>(a, b, br.z, s)];
-      }
-      tot = canon(tot);
-      if (valid) {
-        if (direct) {
-          oi[s] = s;
-          if (ov) ov[s] = tot;
-        } else {
-          row[s] = tot;
-          vmin = fminf(vmin, tot);
-          vmax = fmaxf(vmax, tot);
-        }
+  // results of tile t: lanes 0-31 carry keys t*32 + lane
+  auto emit = [&](int t, float tot) {
+    const int s = t * kPipeKeys + lane;
+    if (lane < 32 && s < lim) {
+      if constexpr (QK == DT_FP8) tot *= a.k_descale[key_slot<PAGED>(a, b, br.z, s)];
+      if (direct) {
+        oi[s] = s;
+        if (ov) ov[s] = tot + 0.0f;        // -0 -> +0
+      } else {
+        row[s] = canon(tot);
       }
     }
+  };
+
+  constexpr int D = kStageDepth;
+  PipeStage<QK, PAGED, NT, D> st;
+  f32x16 accA[MB], accB[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    accA[mb] = f32x16{};
+    accB[mb] = f32x16{};
+  }
+  if (ntiles > 0) {
+    st.template load<0>(a, b, br.z, 0, kend, tid);
+    st.template load<1>(a, b, br.z, kPipeKeys, kend, tid);
+    if constexpr (D > 2) {
+      st.template load<2 % D>(a, b, br.z, 2 * kPipeKeys, kend, tid);
+      st.template load<3 % D>(a, b, br.z, 3 * kPipeKeys, kend, tid);
+    }
+    st.template store<0>(smem, tid);
+  }
+  __syncthreads();
+
+  // Step t (ring set S = t % D): store tile t+1 into the other LDS buffer, load
+  // tile t+D into set S, MFMAs of tile t into `cur` interleaved with the
+  // epilogue of tile t-1 from `prev`.
+  auto step = [&](auto set, int t, f32x16 (&cur)[MB], const f32x16 (&prev)[MB]) {
+    constexpr int S = decltype(set)::value;
+    st.template store<(S + 1) % D>(smem + ((t + 1) & 1) * TILE, tid);
+    st.template load<S>(a, b, br.z, (t + D) * kPipeKeys, kend, tid);
+    F kb[M::KSTEPS];
+    read_tile_frags<QK>(smem + (t & 1) * TILE, lane, kb);
+    mma_tile<QK, MB>(qf, kb, cur);
+    const float prev_score = block_score<MB>(prev, wv);
+    pipe_schedule<QK, MB>();
+    if (t > 0) emit(t - 1, prev_score);
+    __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 4) {     // body unrolled 4x (two accumulator sets x ring)
+    step(IntC<0>(), t, accA, accB);
+    if (t + 1 < ntiles) step(IntC<1>(), t + 1, accB, accA);
+    if (t + 2 < ntiles) step(IntC<2 % D>(), t + 2, accA, accB);
+    if (t + 3 < ntiles) step(IntC<3 % D>(), t + 3, accB, accA);
+  }
+  if (ntiles > 0) {
+    const int last = ntiles - 1;
+    emit(last, (last & 1) ? block_score<MB>(accB, wv) : block_score<MB>(accA, wv));
   }
   __syncthreads();                         // the tile area becomes select scratch
   if (!has_row) return;
@@ -134,10 +173,16 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void dense_kernel(KArgs a) {
   }
   uint32_t* hist = reinterpret_cast<uint32_t*>(smem + wave * kWaveScratch);
   uint32_t* scr = hist + 256;
+  float vmin = __builtin_inff(), vmax = -__builtin_inff();
+  for (int p = lane; p < lim; p += 64) {
+    const float f = row[p];
+    vmin = fminf(vmin, f);
+    vmax = fmaxf(vmax, f);
+  }
   float fb;
   uint32_t eb;
   wave_kth(row, nullptr, lim, topk, wave_min_f(vmin), wave_max_f(vmax), hist, scr, fb, eb);
-  write_kept(row, nullptr, lim, fb, eb, oi, ov);
+  write_kept(row, nullptr, lim, fb, eb, oi, ov, topk);
 }
 
 // ---------------------------------------------------------------------------
@@ -228,7 +273,7 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_kernel(KArgs a) {
             kept += __popcll(km);
             wave_sync();
           }
-          count = kept;
+          count = kept < topk ? kept : topk;   // exactly topk for ordered scores
           thr = fb;
           vmax = wave_max_f(vmax);
           vmin = fb;
@@ -259,7 +304,7 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_kernel(KArgs a) {
     float fb;
     uint32_t eb;
     wave_kth(listF, listI, count, topk, wave_min_f(vmin), wave_max_f(vmax), hist, scr, fb, eb);
-    write_kept(listF, listI, count, fb, eb, oi, ov);
+    write_kept(listF, listI, count, fb, eb, oi, ov, topk);
     n = topk;
   } else {
     for (int e = lane; e < count; e += 64) {
