@@ -35,9 +35,45 @@ PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp8": 5033.2}   # dense MFMA, MI
 PEAK_HBM_GBS = 8000.0
 HBM_BOUND = {"decode"}
 
-# measured rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dominant
-# kernel for the default workload, scaled by the plain-copy calibration; None until taken
-TRAFFIC_BYTES = {}
+# HBM traffic of the dominant kernel per launch, from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE runs scaled by the same counters on a plain copy of known size.  Kept in
+# profiles/traffic.json together with a hash of the kernel sources it was measured on;
+# reported only while the sources still match (null otherwise).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["li_device.h", "li_common_kernels.h", "li_pipe.h", "li_select.h",
+                  "li_prefill.hip", "li_decode.hip", "li_metadata.hip", "li_host.cpp",
+                  "li_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "score_top_token_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def copy_calibration(nbytes: int, reps: int) -> None:
+    """A plain device-to-device copy of nbytes, reps times (the counter calibration)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def visible_pairs(inst) -> int:
@@ -58,7 +94,7 @@ def algorithmic_bytes(inst) -> int:
     rows = sum(inst["seqlens_q"])
     q = rows * inst["n1"] * 128 * esz
     w = rows * inst["n1"] * (4 if inst["w_dtype"] == "fp32" else 2)
-    keys = sum(min(s2, s2 if inst["mask_mode"] == 0 else s2) for s2 in inst["seqlens_k"])
+    keys = sum(inst["seqlens_k"])            # every key is visible to some row
     k = keys * 128 * esz
     extra = 0
     if inst["qk_dtype"] == "fp8":
@@ -105,7 +141,16 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (counter calibration) and exit")
+    ap.add_argument("--print-kernel-hash", action="store_true")
     args = ap.parse_args()
+    if args.print_kernel_hash:
+        print(kernel_source_hash())
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 4)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
@@ -192,12 +237,12 @@ def main():
     if args.workload in HBM_BOUND:
         achieved = hbm / (fwd_avg / 1000.0) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": TRAFFIC_BYTES.get(args.workload)}
+                "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.workload)}
     else:
         achieved = flop / (fwd_avg / 1000.0) / 1e12
         peak = PEAK_TFLOPS[dtype]
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": TRAFFIC_BYTES.get(args.workload)}
+                "frac": achieved / peak, "traffic": measured_traffic(args.workload)}
 
     cfg = {"workload": args.workload, "batch": inst["batch"], "seq_len_q": inst["max_seqlen_q"],
            "seq_len_k": inst["max_seqlen_k"], "query_rows": rows, "heads_q": inst["n1"],
