@@ -3,112 +3,109 @@
 // A handful of query rows cannot fill 256 compute units row by row, so the
 // visible keys of all rows are cut into segments of about equal length (the
 // work items of the metadata kernel).  The split kernel streams each segment of
-// K from HBM once, straight into MFMA B operands (every K byte is used by one
-// row only, so there is no LDS round trip), double-buffered in registers so the
-// next tile's loads are in flight while the current tile is scored, applies the
-// ReLU / weight / head-sum epilogue and stores each key's score into a dense
-// per-row fp32 array in the workspace.  The select kernel then runs one
+// K from HBM once with coalesced loads, several tiles ahead of the compute,
+// turns each tile into MFMA B operands through a per-wave LDS buffer, applies
+// the ReLU / weight / head-sum epilogue and stores each key's score into a
+// dense per-row fp32 array in the workspace.  The select kernel then runs one
 // workgroup per row: the exact bucket select of the k-th element (value
-// descending, smaller key first on ties) over the row held in LDS, and a stable
+// descending, smaller key first on ties) over the row held in registers, and a stable
 // write of the top-k in ascending key order, padded with -1 / -inf.
 //
 // The score follows the npu_lightning_indexer_pto page (formula under "功能说明")
 // and the lightning_indexer page ("Function" steps 1-3, Constraints for the
 // padding); paged keys are read through block_table (npu_lightning_indexer_pto
 // page, block_table parameter).
-#include "li_common_kernels.h"
+#include "li_pipe.h"
 #include "li_select.h"
 
 namespace li {
 
 namespace {
 
-template <int QK, bool PAGED>
-__device__ inline void load_key_frags(const KArgs& a, int b, int k_off, int base, int k1, int lane,
-                                      typename Mma<QK>::frag (&kf)[2][Mma<QK>::KSTEPS],
-                                      int64_t& slot) {
-  typedef Mma<QK> M;
-  slot = 0;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int s = base + nb * 32 + (lane & 31);
-    if (s < k1) {
-      const unsigned char* row = key_row<QK, PAGED>(a, b, k_off, s);
-#pragma unroll
-      for (int j = 0; j < M::KSTEPS; ++j) kf[nb][j] = load_frag_global<QK>(row + frag_off<QK>(lane, j));
-      // lane l reports key base + l: column l % 32 of block l / 32
-      if constexpr (QK == DT_FP8) {
-        if (nb == (lane >> 5)) slot = key_slot<PAGED>(a, b, k_off, s);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < M::KSTEPS; ++j) kf[nb][j] = zero_frag<QK>();
-    }
-  }
-}
+constexpr int kDecodeDepth = 4;   // 32-key tiles in flight per wave (even)
 
-template <int QK, int MB>
-__device__ inline float score_tile_regs(const typename Mma<QK>::frag (&qf)[MB][Mma<QK>::KSTEPS],
-                                        const typename Mma<QK>::frag (&kf)[2][Mma<QK>::KSTEPS],
-                                        const float (&wv)[MB][16], int lane) {
-  typedef Mma<QK> M;
-  f32x16 acc[MB][2];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    acc[mb][0] = f32x16{};
-    acc[mb][1] = f32x16{};
-  }
-#pragma unroll
-  for (int j = 0; j < M::KSTEPS; ++j)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = M::mma(qf[mb][j], kf[nb][j], acc[mb][nb]);
-  return head_sum<MB>(acc, wv, lane);
-}
-
-// One wave per segment (item): waves of a workgroup work independently.
-template <int QK, int MB, int WT, bool PAGED>
+// One wave per segment (item); the waves of a workgroup work independently.
+// The segment's K streams through a ring of kDecodeDepth register sets filled
+// by coalesced 16-byte loads (a 1 KiB run of K per instruction), so about
+// kDecodeDepth * 32 keys are in flight per wave.  Each tile passes through the
+// wave's own LDS buffer to reach the MFMA operand layout; its MFMAs are
+// interleaved with the epilogue of the previous tile.
+template <int QK, int MB, int WT, int KL>
 __global__ __launch_bounds__(kDecodeWaves * 64, 1) void split_kernel(KArgs a) {
   typedef Mma<QK> M;
   typedef typename M::frag F;
-  constexpr int STEP = kTileKeys;
+  constexpr int D = kDecodeDepth;
+  constexpr int TILE = kPipeKeys * M::RB;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const MetaHeader* hdr = reinterpret_cast<const MetaHeader*>(a.meta);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int it = blockIdx.x * kDecodeWaves + wave;
   if (it >= hdr->n_items) return;
   const int4 item = reinterpret_cast<const int4*>(a.meta + a.off_items)[it];
   const int b = item.x, i = item.y, k0 = item.z, k1 = item.w;
   const int4 br = batch_rec(a, b);
   const int64_t tok = (int64_t)br.x + i;
+  unsigned char* tile = smem + wave * TILE;
 
   F qf[MB][M::KSTEPS];
   float wv[MB][16];
   load_query<QK, MB, WT>(a, tok, lane, qf, wv);
   float* dst = a.ws + ((int64_t)b * a.s1max + i) * a.ws_row_stride;
 
-  auto finish = [&](int base, float tot, int64_t slot) {
-    const int s = base + lane;
-    if (s < k1) {
-      if constexpr (QK == DT_FP8) tot *= a.k_descale[slot];
+  // score of tile t: lanes 0-31 carry keys k0 + 32 t + lane
+  auto emit = [&](int t, float tot, float ds) {
+    const int s = k0 + t * kPipeKeys + lane;
+    if (lane < 32 && s < k1) {
+      if constexpr (QK == DT_FP8) tot *= ds;
       // -0 -> +0; NaN (only from NaN inputs) -> -inf keeps the scores ordered
       dst[s] = tot == 0.0f ? 0.0f : (tot != tot ? -__builtin_inff() : tot);
     }
   };
 
-  F ka[2][M::KSTEPS], kb[2][M::KSTEPS];
-  int64_t sa = 0, sb = 0;
-  int base = k0;
-  if (base < k1) load_key_frags<QK, PAGED>(a, b, br.z, base, k1, lane, ka, sa);
-  while (base < k1) {
-    if (base + STEP < k1) load_key_frags<QK, PAGED>(a, b, br.z, base + STEP, k1, lane, kb, sb);
-    finish(base, score_tile_regs<QK, MB>(qf, ka, wv, lane), sa);
-    base += STEP;
-    if (base >= k1) break;
-    if (base + STEP < k1) load_key_frags<QK, PAGED>(a, b, br.z, base + STEP, k1, lane, ka, sa);
-    finish(base, score_tile_regs<QK, MB>(qf, kb, wv, lane), sb);
-    base += STEP;
+  if (k0 >= k1) return;
+  const int ntiles = (k1 - k0 + kPipeKeys - 1) / kPipeKeys;
+  PipeStage<QK, KL, 64, D> st;
+  f32x16 accA[MB], accB[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    accA[mb] = f32x16{};
+    accB[mb] = f32x16{};
   }
+  static_for<D>([&](auto set) {
+    constexpr int S = decltype(set)::value;
+    st.template load<S>(a, b, br.z, k0 + S * kPipeKeys, k1, lane);
+  });
+  float dprev = 1.0f;
+
+  // Step t (ring set S = t % D): tile t from set S into LDS, refill set S with
+  // tile t + D, MFMAs of tile t into one accumulator set interleaved with the
+  // epilogue of tile t - 1 from the other.
+  auto step = [&](auto set, int t) {
+    constexpr int S = decltype(set)::value;
+    f32x16(&cur)[MB] = (S & 1) ? accB : accA;
+    f32x16(&prev)[MB] = (S & 1) ? accA : accB;
+    st.template store<S>(tile, lane);
+    const float dcur = st.dsc[S];
+    st.template load<S>(a, b, br.z, k0 + (t + D) * kPipeKeys, k1, lane);
+    wave_sync();
+    F kb[M::KSTEPS];
+    read_tile_frags<QK>(tile, lane, kb);
+    mma_tile<QK, MB>(qf, kb, cur);
+    const float prev_score = block_score<MB>(prev, wv);
+    pipe_schedule<QK, MB>();
+    if (t > 0) emit(t - 1, prev_score, dprev);
+    dprev = dcur;
+    wave_sync();
+  };
+  // Full groups of D steps run unconditionally, so every step issues the same
+  // loads and the ring never drains; the last tiles follow one by one.
+  int t = 0;
+  for (; t + D <= ntiles; t += D) static_for<D>([&](auto set) { step(set, t + decltype(set)::value); });
+  static_for<D - 1>([&](auto set) {
+    if (t + decltype(set)::value < ntiles) step(set, t + decltype(set)::value);
+  });
+  const int last = ntiles - 1;
+  emit(last, (last & 1) ? block_score<MB>(accB, wv) : block_score<MB>(accA, wv), dprev);
 }
 
 // ---------------------------------------------------------------------------
@@ -121,8 +118,13 @@ struct SelShared {
   int misc[64];           // 0: bucket, 1: above, 2: count, 3: gathered, 4..5: fb/eb, 8..: scan
   float cand_f[kSelSmall];
   uint32_t cand_e[kSelSmall];
-  uint32_t hist[kNB];
+  uint32_t hist[kNB + 64];   // + one discard bin per lane, so skipped elements never collide
 };
+
+// histogram slot of an element: its bucket, or the lane's discard bin
+__device__ inline uint32_t hist_slot(bool in, uint32_t bucket) {
+  return in ? bucket : (uint32_t)kNB + (threadIdx.x & 63);
+}
 
 __device__ inline float block_min_f(float v, int* tmp) {
   v = wave_min_f(v);
@@ -179,6 +181,107 @@ __device__ inline int block_wave_prefix(int v, int* tmp, int* total) {
   return before;
 }
 
+// ---------------------------------------------------------------------------
+// Row views.  The select reaches the scores of a row through two traversals:
+//   each(f)    : f(e, valid, v) covering every element e of the row once (with
+//                valid set) in any order, plus padding calls with valid false;
+//   ordered(f) : wave w walks its contiguous segment of the row in index order,
+//                64 elements per step, calling f(p, valid, v) with lane l
+//                holding element p = step start + l.
+// The segment of wave w is [w * seg, min(n, (w + 1) * seg)), seg a multiple of
+// 64 of about n / 16.
+// ---------------------------------------------------------------------------
+__device__ inline int sel_segment(int n) { return ((n + kSelWaves - 1) / kSelWaves + 63) / 64 * 64; }
+
+// A row of at most kRegRowMax elements held in registers: lane l of wave w
+// holds elements w * seg + 64 j + l, j < kRegSteps.  Every pass then runs
+// without memory reads, its loop fully unrolled into straight-line code.
+// Slots past the wave's segment hold a quiet NaN: scores are never NaN (the
+// split kernel stores NaN as -inf), a NaN is ignored by fminf / fmaxf, fails
+// every comparison and its order-preserving key lies above that of +inf, so
+// most passes need no validity test at all.
+constexpr int kRegSteps = 32;
+constexpr int kRegRowMax = kRegSteps * 64 * kSelWaves;   // 32768
+
+struct RegRow {
+  float v[kRegSteps];
+  int e0;           // this lane's element of step 0
+  int steps;        // steps holding elements of this wave's segment (uniform)
+
+  __device__ __forceinline__ void load(const float* src, int n) {
+    const int w = threadIdx.x >> 6, seg = sel_segment(n);
+    const int s1 = min(n, w * seg + seg);
+    e0 = w * seg + (threadIdx.x & 63);
+    steps = __builtin_amdgcn_readfirstlane(s1 > w * seg ? (s1 - w * seg + 63) / 64 : 0);
+#pragma unroll
+    for (int j = 0; j < kRegSteps; ++j) {
+      const int e = e0 + 64 * j;
+      const float f = src[min(e, n - 1)];           // in bounds for every lane
+      v[j] = e < s1 ? f : __builtin_nanf("");
+    }
+  }
+  template <class F>
+  __device__ __forceinline__ void each(F f) const {
+#pragma unroll
+    for (int j = 0; j < kRegSteps; ++j)
+      if (j < steps) f(e0 + 64 * j, v[j] == v[j], v[j]);
+  }
+  // the scheduling barrier keeps the compiler from computing the lane masks of
+  // all steps up front, which would not fit in scalar registers
+  template <class F>
+  __device__ __forceinline__ void ordered(F f) const {
+#pragma unroll
+    for (int j = 0; j < kRegSteps; ++j) {
+      if (j < steps) f(e0 + 64 * j, v[j] == v[j], v[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
+// A row read from the workspace (rows longer than kRegRowMax).  The loads of
+// kSelUnroll elements are issued before any call, so their latencies overlap.
+constexpr int kSelUnroll = 8;
+struct GlobalRow {
+  const float* vals;
+  int n;
+
+  template <class F>
+  __device__ __forceinline__ void each(F f) const {
+    for (int e0 = threadIdx.x; e0 < n; e0 += kSelUnroll * kSelectThreads) {
+      float v[kSelUnroll];
+#pragma unroll
+      for (int u = 0; u < kSelUnroll; ++u) {
+        const int e = e0 + u * kSelectThreads;
+        v[u] = e < n ? vals[e] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kSelUnroll; ++u) {
+        const int e = e0 + u * kSelectThreads;
+        f(e, e < n, v[u]);
+      }
+    }
+  }
+  template <class F>
+  __device__ __forceinline__ void ordered(F f) const {
+    const int seg = sel_segment(n);
+    const int s0 = (threadIdx.x >> 6) * seg, s1 = min(n, s0 + seg);
+    const int l = threadIdx.x & 63;
+    for (int p0 = s0; p0 < s1; p0 += 4 * 64) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int p = p0 + u * 64 + l;
+        v[u] = p < s1 ? vals[p] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int p = p0 + u * 64 + l;
+        if (p0 + u * 64 < s1) f(p, p < s1, v[u]);
+      }
+    }
+  }
+};
+
 // Bucket of the element of rank r from the top of hist[0, kNB): thread t owns
 // buckets 2t, 2t+1.  Writes bucket / above / count to sh.misc[0..2].
 __device__ inline void block_find_bucket(SelShared& sh, int r) {
@@ -234,20 +337,24 @@ struct UBucketN {
 
 // gathers the (<= kSelSmall) candidates with in(f) into sh.cand_*, then wave 0
 // ranks them; the k-th element lands in sh.misc[4..5]
-template <class Pred>
-__device__ inline void block_gather_rank(SelShared& sh, const float* vals, int n, int r, Pred in) {
+template <class Row, class Pred>
+__device__ __forceinline__ void block_gather_rank(SelShared& sh, const Row& row, int r, Pred in) {
   if (threadIdx.x == 0) sh.misc[3] = 0;
   __syncthreads();
-  for (int e = threadIdx.x; e < n; e += kSelectThreads) {
-    const float f = vals[e];
-    if (in(f)) {
-      const int slot = atomicAdd(&sh.misc[3], 1);
-      if (slot < kSelSmall) {
+  row.each([&](int e, bool valid, float f) {
+    const bool take = valid & in(f);
+    const uint64_t m = ballot(take);
+    if (m != 0) {                          // uniform: one slot reservation per wave
+      int base = 0;
+      if ((threadIdx.x & 63) == __builtin_ctzll(m)) base = atomicAdd(&sh.misc[3], __popcll(m));
+      base = __shfl(base, (int)__builtin_ctzll(m));
+      const int slot = base + mbcnt(m);
+      if (take && slot < kSelSmall) {
         sh.cand_f[slot] = f;
         sh.cand_e[slot] = (uint32_t)e;
       }
     }
-  }
+  });
   __syncthreads();
   if (threadIdx.x < 64) {
     const int m = min(sh.misc[3], kSelSmall);
@@ -266,46 +373,37 @@ __device__ inline void block_gather_rank(SelShared& sh, const float* vals, int n
 }
 
 // the r-th entry (index order) whose key equals u; writes fb / eb into sh.misc[4..5]
-__device__ inline void block_rth_equal(SelShared& sh, const float* vals, int n, int r, uint32_t u) {
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int seg = ((n + kSelWaves - 1) / kSelWaves + 63) / 64 * 64;
-  const int e0 = w * seg, e1 = min(n, e0 + seg);
+template <class Row>
+__device__ __forceinline__ void block_rth_equal(SelShared& sh, const Row& row, int r, uint32_t u) {
   int cnt = 0;
-  for (int p0 = e0; p0 < e1; p0 += 64) {
-    const int p = p0 + l;
-    cnt += __popcll(ballot(p < e1 && f2key(vals[p]) == u));
-  }
+  row.ordered([&](int, bool valid, float f) { cnt += __popcll(ballot(valid & (f2key(f) == u))); });
   const int before = block_wave_prefix(cnt, sh.misc + 8, nullptr);
   if (before < r && r <= before + cnt) {
     int seen = before;
-    for (int p0 = e0; p0 < e1; p0 += 64) {
-      const int p = p0 + l;
-      const bool eq = p < e1 && f2key(vals[p]) == u;
+    row.ordered([&](int p, bool valid, float f) {
+      const bool eq = valid & (f2key(f) == u);
       const uint64_t m = ballot(eq);
-      if (seen + __popcll(m) >= r) {
-        if (eq && seen + mbcnt(m) == r - 1) {
-          sh.misc[4] = (int)u;
-          sh.misc[5] = p;
-        }
-        break;
-      }
+      // exactly one lane of the whole pass sees itself as the r-th equal entry
+      if (eq & (seen + mbcnt(m) == r - 1)) sh.misc[5] = p;
       seen += __popcll(m);
-    }
+    });
   }
   __syncthreads();
   if (threadIdx.x == 0) sh.misc[4] = __float_as_int(key2f(u));
   __syncthreads();
 }
 
-// k-th element of vals[0, n) in (value desc, index asc) order -> sh.misc[4..5]
-__device__ void block_kth(SelShared& sh, const float* vals, int n, int k, float lo, float hi) {
+// k-th element of the row in (value desc, index asc) order -> sh.misc[4..5];
+// lo / hi are the row's minimum and maximum
+template <class Row>
+__device__ __forceinline__ void block_kth(SelShared& sh, const Row& row, int k, float lo, float hi) {
   int r = k;
   uint32_t ulo, uhi;
   if (lo < hi) {
     const FBucketN fbk(lo, hi);
     for (int x = threadIdx.x; x < kNB; x += kSelectThreads) sh.hist[x] = 0;
     __syncthreads();
-    for (int e = threadIdx.x; e < n; e += kSelectThreads) atomicAdd(&sh.hist[fbk(vals[e])], 1u);
+    row.each([&](int, bool valid, float f) { atomicAdd(&sh.hist[hist_slot(valid, fbk(f))], 1u); });
     __syncthreads();
     block_find_bucket(sh, r);
     const uint32_t B = (uint32_t)sh.misc[0];
@@ -313,18 +411,16 @@ __device__ void block_kth(SelShared& sh, const float* vals, int n, int k, float 
     r -= above;
     __syncthreads();
     if (cnt <= kSelSmall) {
-      block_gather_rank(sh, vals, n, r, [&](float f) { return fbk(f) == B; });
+      block_gather_rank(sh, row, r, [&](float f) { return fbk(f) == B; });
       return;
     }
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-    for (int e = threadIdx.x; e < n; e += kSelectThreads) {
-      const float f = vals[e];
-      if (fbk(f) == B) {
-        const uint32_t u = f2key(f);
-        mn = min(mn, u);
-        mx = max(mx, u);
-      }
-    }
+    row.each([&](int, bool valid, float f) {
+      const uint32_t u = f2key(f);
+      const bool in = valid & (fbk(f) == B);
+      mn = in ? min(mn, u) : mn;
+      mx = in ? max(mx, u) : mx;
+    });
     ulo = block_min_u(mn, sh.misc + 8);
     uhi = block_max_u(mx, sh.misc + 8);
   } else {
@@ -332,16 +428,17 @@ __device__ void block_kth(SelShared& sh, const float* vals, int n, int k, float 
   }
   for (;;) {
     if (ulo == uhi) {
-      block_rth_equal(sh, vals, n, r, ulo);
+      block_rth_equal(sh, row, r, ulo);
       return;
     }
     const UBucketN ubk(ulo, uhi);
     for (int x = threadIdx.x; x < kNB; x += kSelectThreads) sh.hist[x] = 0;
     __syncthreads();
-    for (int e = threadIdx.x; e < n; e += kSelectThreads) {
-      const uint32_t u = f2key(vals[e]);
-      if (u >= ulo && u <= uhi) atomicAdd(&sh.hist[ubk(u)], 1u);
-    }
+    row.each([&](int, bool valid, float f) {
+      const uint32_t u = f2key(f);
+      const bool in = valid & (u >= ulo) & (u <= uhi);
+      atomicAdd(&sh.hist[hist_slot(in, ubk(u))], 1u);
+    });
     __syncthreads();
     block_find_bucket(sh, r);
     const int B = sh.misc[0], above = sh.misc[1], cnt = sh.misc[2];
@@ -351,9 +448,9 @@ __device__ void block_kth(SelShared& sh, const float* vals, int n, int k, float 
     uint32_t nhi = (B == kNB - 1) ? uhi : nlo + ((1u << ubk.shift) - 1u);
     if (nhi > uhi) nhi = uhi;
     if (cnt <= kSelSmall && nlo != nhi) {
-      block_gather_rank(sh, vals, n, r, [&](float f) {
+      block_gather_rank(sh, row, r, [&](float f) {
         const uint32_t u = f2key(f);
-        return u >= nlo && u <= nhi;
+        return (u >= nlo) & (u <= nhi);
       });
       return;
     }
@@ -362,16 +459,40 @@ __device__ void block_kth(SelShared& sh, const float* vals, int n, int k, float 
   }
 }
 
+// k-th element and stable, index-ordered write of the top-k of one row.
+template <class Row>
+__device__ __forceinline__ void select_row(SelShared& sh, const Row& row, int topk, float lo,
+                                           float hi, int32_t* oi, float* ov) {
+  block_kth(sh, row, topk, lo, hi);
+  const float fb = __int_as_float(sh.misc[4]);
+  const uint32_t eb = (uint32_t)sh.misc[5];
+  __syncthreads();
+  int kept = 0;
+  row.ordered([&](int p, bool valid, float f) {
+    kept += __popcll(ballot(valid & ((f > fb) | ((f == fb) & ((uint32_t)p <= eb)))));
+  });
+  int pos = block_wave_prefix(kept, sh.misc + 8, nullptr);
+  const bool has_ov = ov != nullptr;
+  row.ordered([&](int p, bool valid, float f) {
+    const bool keep = valid & ((f > fb) | ((f == fb) & ((uint32_t)p <= eb)));
+    const uint64_t m = ballot(keep);
+    const int o = pos + mbcnt(m);
+    const bool st = keep & (o < topk);     // bounded whatever the data
+    if (st) oi[o] = p;
+    if (st & has_ov) ov[o] = f;
+    pos += __popcll(m);
+  });
+}
+
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(KArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   SelShared& sh = *reinterpret_cast<SelShared*>(smem);
-  float* cache = reinterpret_cast<float*>(smem + sizeof(SelShared));
   const int r = blockIdx.x;
   const int b = r / a.s1max, i = r - (r / a.s1max) * a.s1max;
   if (b >= a.batch) return;
   const int4 br = batch_rec(a, b);
   if (i >= br.y) return;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int tid = threadIdx.x;
   const int lim = visible_limit(a.mask_mode, i, br.y, br.w);
   const int topk = a.topk;
   const int64_t tok = (int64_t)br.x + i;
@@ -391,91 +512,68 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(KArgs a) {
     }
     return;
   }
-  const bool cached = lim <= kSelectCacheKeys;
   float mn = __builtin_inff(), mx = -__builtin_inff();
-  for (int e = tid; e < lim; e += kSelectThreads) {
-    const float f = src[e];
-    if (cached) cache[e] = f;
-    mn = fminf(mn, f);
-    mx = fmaxf(mx, f);
-  }
-  const float lo = block_min_f(mn, sh.misc + 8);
-  const float hi = block_max_f(mx, sh.misc + 8);
-  const float* vals = cached ? cache : src;
-  block_kth(sh, vals, lim, topk, lo, hi);
-  const float fb = __int_as_float(sh.misc[4]);
-  const uint32_t eb = (uint32_t)sh.misc[5];
-  __syncthreads();
-
-  // stable write: each wave owns a contiguous, 64-aligned segment of the row
-  const int seg = ((lim + kSelWaves - 1) / kSelWaves + 63) / 64 * 64;
-  const int e0 = w * seg, e1 = min(lim, e0 + seg);
-  int kept = 0;
-  for (int p0 = e0; p0 < e1; p0 += 64) {
-    const int p = p0 + l;
-    bool keep = false;
-    if (p < e1) {
-      const float f = vals[p];
-      keep = f > fb || (f == fb && (uint32_t)p <= eb);
-    }
-    kept += __popcll(ballot(keep));
-  }
-  int pos = block_wave_prefix(kept, sh.misc + 8, nullptr);
-  for (int p0 = e0; p0 < e1; p0 += 64) {
-    const int p = p0 + l;
-    float f = 0.0f;
-    bool keep = false;
-    if (p < e1) {
-      f = vals[p];
-      keep = f > fb || (f == fb && (uint32_t)p <= eb);
-    }
-    const uint64_t m = ballot(keep);
-    if (keep) {
-      const int o = pos + mbcnt(m);
-      if (o < topk) {                      // bounded whatever the data
-        oi[o] = p;
-        if (ov) ov[o] = f;
-      }
-    }
-    pos += __popcll(m);
+  if (lim <= kRegRowMax) {
+    RegRow row;
+    row.load(src, lim);
+    row.each([&](int, bool, float f) {   // padding NaNs are ignored by fminf / fmaxf
+      mn = fminf(mn, f);
+      mx = fmaxf(mx, f);
+    });
+    const float lo = block_min_f(mn, sh.misc + 8);
+    const float hi = block_max_f(mx, sh.misc + 8);
+    select_row(sh, row, topk, lo, hi, oi, ov);
+  } else {
+    const GlobalRow row{src, lim};
+    row.each([&](int, bool valid, float f) {
+      mn = valid ? fminf(mn, f) : mn;
+      mx = valid ? fmaxf(mx, f) : mx;
+    });
+    const float lo = block_min_f(mn, sh.misc + 8);
+    const float hi = block_max_f(mx, sh.misc + 8);
+    select_row(sh, row, topk, lo, hi, oi, ov);
   }
 }
 
-template <int QK, int MB, int WT, bool PAGED>
+template <int QK, int MB, int WT, int KL>
 hipError_t launch_split(const KArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((split_kernel<QK, MB, WT, PAGED>), dim3(grid), dim3(kDecodeWaves * 64), 0, s, a);
+  constexpr size_t lds = (size_t)kDecodeWaves * kPipeKeys * Mma<QK>::RB;   // one K tile per wave
+  hipLaunchKernelGGL((split_kernel<QK, MB, WT, KL>), dim3(grid), dim3(kDecodeWaves * 64), lds, s, a);
   return hipGetLastError();
 }
 
 template <int QK, int MB, int WT>
-hipError_t launch_split_p(const KArgs& a, bool paged, int grid, hipStream_t s) {
-  return paged ? launch_split<QK, MB, WT, true>(a, grid, s)
-               : launch_split<QK, MB, WT, false>(a, grid, s);
+hipError_t launch_split_p(const KArgs& a, int kl, int grid, hipStream_t s) {
+  switch (kl) {
+    case KL_CONTIG: return launch_split<QK, MB, WT, KL_CONTIG>(a, grid, s);
+    case KL_PAGED: return launch_split<QK, MB, WT, KL_PAGED>(a, grid, s);
+    default: return launch_split<QK, MB, WT, KL_PAGED_TILE>(a, grid, s);
+  }
 }
 
 template <int QK, int MB>
-hipError_t launch_split_w(const KArgs& a, int w_dtype, bool paged, int grid, hipStream_t s) {
-  return w_dtype == DT_FP32 ? launch_split_p<QK, MB, DT_FP32>(a, paged, grid, s)
-                            : launch_split_p<QK, MB, DT_BF16>(a, paged, grid, s);
+hipError_t launch_split_w(const KArgs& a, int w_dtype, int kl, int grid, hipStream_t s) {
+  return w_dtype == DT_FP32 ? launch_split_p<QK, MB, DT_FP32>(a, kl, grid, s)
+                            : launch_split_p<QK, MB, DT_BF16>(a, kl, grid, s);
 }
 
 template <int QK>
-hipError_t launch_split_mb(const KArgs& a, int w_dtype, int mblocks, bool paged, int grid,
+hipError_t launch_split_mb(const KArgs& a, int w_dtype, int mblocks, int kl, int grid,
                            hipStream_t s) {
-  return mblocks == 1 ? launch_split_w<QK, 1>(a, w_dtype, paged, grid, s)
-                      : launch_split_w<QK, 2>(a, w_dtype, paged, grid, s);
+  return mblocks == 1 ? launch_split_w<QK, 1>(a, w_dtype, kl, grid, s)
+                      : launch_split_w<QK, 2>(a, w_dtype, kl, grid, s);
 }
 
 }  // namespace
 
 size_t select_shared_bytes() { return sizeof(SelShared); }
 
-hipError_t launch_decode(const KArgs& a, int qk_dtype, int w_dtype, int mblocks, bool paged,
+hipError_t launch_decode(const KArgs& a, int qk_dtype, int w_dtype, int mblocks, int kl,
                          int grid, hipStream_t s) {
   switch (qk_dtype) {
-    case DT_BF16: return launch_split_mb<DT_BF16>(a, w_dtype, mblocks, paged, grid, s);
-    case DT_FP16: return launch_split_mb<DT_FP16>(a, w_dtype, mblocks, paged, grid, s);
-    case DT_FP8: return launch_split_mb<DT_FP8>(a, w_dtype, mblocks, paged, grid, s);
+    case DT_BF16: return launch_split_mb<DT_BF16>(a, w_dtype, mblocks, kl, grid, s);
+    case DT_FP16: return launch_split_mb<DT_FP16>(a, w_dtype, mblocks, kl, grid, s);
+    case DT_FP8: return launch_split_mb<DT_FP8>(a, w_dtype, mblocks, kl, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

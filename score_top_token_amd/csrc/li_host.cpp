@@ -100,8 +100,7 @@ li_status make_plan(const li_problem* p, Plan* pl) {
     items = 3 * (int64_t)B * p->max_seqlen_q + kDecodeSegments;
     pl->ws_row_stride = (int64_t)align_up(p->max_seqlen_k, 64);
     pl->ws_bytes = (size_t)B * p->max_seqlen_q * pl->ws_row_stride * 4;
-    const int cache = std::min(p->max_seqlen_k, kSelectCacheKeys);
-    pl->lds_select = select_shared_bytes() + (size_t)cache * 4;
+    pl->lds_select = select_shared_bytes();
   } else if (dense_lds <= kLdsBudget) {
     pl->mode = kModeDense;
     pl->rows_per_item = kDenseWaves;
@@ -253,12 +252,14 @@ li_status li_forward(const li_problem* p, const void* q, const void* k, const vo
   a.out_idx = sparse_indices;
   a.out_val = sparse_values;
   const int qk = p->qk_dtype, wt = p->w_dtype;
-  const bool paged = p->layout_k == LI_LAYOUT_PA_BSND;
+  // paged blocks holding whole 32-key tiles let a tile be addressed by one lookup
+  const int kl = p->layout_k != LI_LAYOUT_PA_BSND ? KL_CONTIG
+                 : (p->block_size % 32 == 0 ? KL_PAGED_TILE : KL_PAGED);
   hipError_t e;
   if (pl.mode != kModeDecode) {
-    e = launch_prefill(a, pl.mode, qk, wt, pl.mblocks, paged, pl.max_items, pl.lds_prefill, stream);
+    e = launch_prefill(a, pl.mode, qk, wt, pl.mblocks, kl, pl.max_items, pl.lds_prefill, stream);
   } else {
-    e = launch_decode(a, qk, wt, pl.mblocks, paged,
+    e = launch_decode(a, qk, wt, pl.mblocks, kl,
                       (int)cdiv64(pl.max_items, kDecodeWaves), stream);
     if (e == hipSuccess)
       e = launch_select(a, p->batch * p->max_seqlen_q, pl.lds_select, stream);

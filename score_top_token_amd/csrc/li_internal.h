@@ -19,7 +19,6 @@ constexpr int kDecodeMaxRows = 4;       // decode mode: at most this many query 
 constexpr int kDecodeWaves = 4;         // decode split kernel: waves per workgroup
 constexpr int kDecodeSegments = 1024;   // decode: key segments per pass (256 CUs x 4 waves)
 constexpr int kSelectThreads = 1024;    // decode-mode select kernel
-constexpr int kSelectCacheKeys = 32768; // decode-mode select: rows up to this length sit in LDS
 constexpr int kSelectBuckets = 2048;    // decode-mode select: histogram buckets
 constexpr size_t kLdsBudget = 160 * 1024;
 constexpr int kWaveScratch = 256 * 4 + 2 * 64 * 4;   // per-wave select scratch: histogram + gather
@@ -89,15 +88,18 @@ struct KArgs {
 
 // Layout / dtype codes as in li.h.
 enum { L_BSND = 0, L_TND = 1, L_PA = 2 };
+// How a kernel addresses K: contiguous tokens, a paged pool, or a paged pool
+// whose block size is a multiple of 32 keys (a 32-key tile never spans blocks).
+enum { KL_CONTIG = 0, KL_PAGED = 1, KL_PAGED_TILE = 2 };
 enum { DT_BF16 = 0, DT_FP8 = 1, DT_FP32 = 2, DT_FP16 = 3 };
 
 // Launchers (defined in the .hip files); return the hipGetLastError() of the launch.
 hipError_t launch_metadata(const KArgs& a, int mode, hipStream_t s);
 hipError_t launch_prefill(const KArgs& a, int mode, int qk_dtype, int w_dtype, int mblocks,
-                          bool paged, int grid, size_t lds, hipStream_t s);
-hipError_t launch_decode(const KArgs& a, int qk_dtype, int w_dtype, int mblocks, bool paged,
+                          int kl, int grid, size_t lds, hipStream_t s);
+hipError_t launch_decode(const KArgs& a, int qk_dtype, int w_dtype, int mblocks, int kl,
                          int grid, hipStream_t s);
 hipError_t launch_select(const KArgs& a, int grid, size_t lds, hipStream_t s);
-size_t select_shared_bytes();   // fixed LDS of the select kernel (before the row cache)
+size_t select_shared_bytes();   // LDS of the select kernel
 
 }  // namespace li

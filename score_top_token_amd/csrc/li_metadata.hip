@@ -7,11 +7,12 @@
 //   - prefill modes: one item per block of `rows_per_item` query rows, ordered so
 //     that the costliest blocks (the last rows of each sequence under right-down
 //     causal masking) are dispatched first, round-robin over the batches;
-//   - decode mode: the visible keys of every query row cut into segments of equal
-//     length (about kDecodeSegments segments in total), one item per segment.
+//   - decode mode: the visible keys of every query row cut into segments of one
+//     length, the shortest for which all rows together need at most
+//     kDecodeSegments segments; one item per segment.
 // The result depends only on the lengths (deterministic) and is produced on the
 // device, so the call never synchronises with the host.
-#include "li_common_kernels.h"
+#include "li_pipe.h"
 
 namespace li {
 
@@ -19,14 +20,30 @@ namespace {
 
 constexpr int kMetaThreads = 1024;
 constexpr int kRoundRobinMaxBatch = 256;
+constexpr int kChunkCands = 8;      // decode: segment lengths tried at once
 
 __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// ceil(a / b) for 0 <= a < 2^53, b > 0: a double-precision quotient (hardware
+// fp64 instead of a long emulated 64-bit integer division), corrected to the
+// exact integer
+__device__ inline long long cdiv64(long long a, long long b) {
+  long long q = (long long)((double)a / (double)b);
+  while (q * b < a) ++q;
+  while (q > 0 && (q - 1) * b >= a) --q;
+  return q;
+}
+
+// SMALL: batch <= kRoundRobinMaxBatch, the batch tables are also kept in LDS
+template <bool SMALL>
 __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mode) {
+  // small batches keep their tables in LDS as well: the later steps read them
+  // from there instead of waiting on global memory round trips
   __shared__ int s_counts[kRoundRobinMaxBatch];
+  __shared__ int s_starts[kRoundRobinMaxBatch];
+  __shared__ int4 s_bt[kRoundRobinMaxBatch];
   __shared__ int s_part[kMetaThreads / 64];
-  __shared__ long long s_vis[kMetaThreads / 64];
-  __shared__ long long s_rows[kMetaThreads / 64];
+  __shared__ unsigned long long s_cand[kChunkCands], s_tot, s_nrows;
   __shared__ int s_total, s_chunk;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int B = a.batch;
@@ -35,6 +52,19 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
   int* counts = reinterpret_cast<int*>(a.meta + a.off_counts);
   int* starts = reinterpret_cast<int*>(a.meta + a.off_starts);
   int4* items = reinterpret_cast<int4*>(a.meta + a.off_items);
+  constexpr bool small = SMALL;
+  auto get_bt = [&](int b) -> int4 {
+    if constexpr (SMALL) return s_bt[b];
+    else return bt[b];
+  };
+  auto get_count = [&](int b) -> int {
+    if constexpr (SMALL) return s_counts[b];
+    else return counts[b];
+  };
+  auto get_start = [&](int b) -> int {
+    if constexpr (SMALL) return s_starts[b];
+    else return starts[b];
+  };
 
   // 1. per-batch lengths (and, for decode, the visible keys of its rows)
   long long vis = 0;
@@ -58,35 +88,66 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
       s2 = a.s2max;
     }
     bt[b] = int4{q_off, s1, k_off, s2};
+    if (small) s_bt[b] = int4{q_off, s1, k_off, s2};
     if (mode == kModeDecode)
       for (int i = 0; i < s1; ++i) vis += visible_limit(a.mask_mode, i, s1, s2);
   }
-  // decode segment length from the total number of visible keys: one segment per
-  // wave of a full GPU (kDecodeSegments, more if there are many rows); every row
-  // adds at most one partial segment, so the count stays within the target.
+  // decode segment length: the shortest multiple of 32 keys for which the
+  // segments of all rows number at most `target` (one per wave of a full GPU,
+  // kDecodeSegments, more if there are many rows).  Since every row adds at
+  // most one partial segment, tot / (target - rows) always fits; the candidates
+  // between tot / target and that bound are counted in one pass.
   if (mode == kModeDecode) {
+    // block sums through LDS atomics (no serial loop over the waves)
+    if (tid < kChunkCands) s_cand[tid] = 0;
+    if (tid == 0) s_tot = s_nrows = 0;
+    __syncthreads();
     long long rows = 0;
-    for (int b = tid; b < B; b += kMetaThreads) rows += bt[b].y;
+    for (int b = tid; b < B; b += kMetaThreads) rows += get_bt(b).y;
     for (int o = 32; o > 0; o >>= 1) {
       vis += __shfl_xor(vis, o);
       rows += __shfl_xor(rows, o);
     }
     if (lane == 0) {
-      s_vis[wave] = vis;
-      s_rows[wave] = rows;
+      atomicAdd(&s_tot, (unsigned long long)vis);
+      atomicAdd(&s_nrows, (unsigned long long)rows);
+    }
+    __syncthreads();
+    const long long tot = (long long)s_tot, nrows = (long long)s_nrows;
+    long long target = kDecodeSegments;
+    while (target < 2 * nrows) target += kDecodeSegments;
+    long long c_hi = (cdiv64(tot, target - nrows) + kPipeKeys - 1) / kPipeKeys * kPipeKeys;
+    long long c_lo = (cdiv64(tot, target) + kPipeKeys - 1) / kPipeKeys * kPipeKeys;
+    if (c_lo < a.chunk) c_lo = a.chunk;
+    if (c_hi < c_lo) c_hi = c_lo;
+    // candidate c_lo + j * step, j < kChunkCands; the last one is c_hi
+    long long step = cdiv64(c_hi - c_lo, kChunkCands - 1);
+    step = (step + kPipeKeys - 1) / kPipeKeys * kPipeKeys;
+    if (step < kPipeKeys) step = kPipeKeys;
+    // thread t counts candidate t % kChunkCands over every
+    // (kMetaThreads / kChunkCands)-th batch; lanes of one candidate are then
+    // summed with three shuffles and one LDS atomic per wave.  lim and c are
+    // below 2^31: 32-bit unsigned division.
+    {
+      const int j = tid % kChunkCands;
+      const uint32_t c = (uint32_t)(j == kChunkCands - 1 ? c_hi : c_lo + j * step);
+      unsigned long long nseg = 0;
+      for (int b = tid / kChunkCands; b < B; b += kMetaThreads / kChunkCands) {
+        const int4 rec = get_bt(b);
+        for (int i = 0; i < rec.y; ++i)
+          nseg += ((uint32_t)visible_limit(a.mask_mode, i, rec.y, rec.w) + c - 1u) / c;
+      }
+      for (int o = kChunkCands; o < 64; o <<= 1) nseg += __shfl_xor(nseg, o);
+      if (lane < kChunkCands && nseg) atomicAdd(&s_cand[lane], nseg);
     }
     __syncthreads();
     if (tid == 0) {
-      long long tot = 0, nrows = 0;
-      for (int w = 0; w < kMetaThreads / 64; ++w) {
-        tot += s_vis[w];
-        nrows += s_rows[w];
+      long long c = c_hi;
+      for (int j = kChunkCands - 1; j >= 0; --j) {
+        const long long cj = j == kChunkCands - 1 ? c_hi : c_lo + j * step;
+        if (cj <= c_hi && (long long)s_cand[j] <= target && cj < c) c = cj;
       }
-      long long target = kDecodeSegments;
-      while (target < 2 * nrows) target += kDecodeSegments;
-      long long c = (tot + (target - nrows) - 1) / (target - nrows);
-      c = (c + kTileKeys - 1) / kTileKeys * kTileKeys;
-      s_chunk = (int)(c > a.chunk ? c : a.chunk);
+      s_chunk = (int)c;
     }
   } else if (tid == 0) {
     s_chunk = a.chunk;
@@ -95,7 +156,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
   const int chunk = s_chunk;
 
   for (int b = tid; b < B; b += kMetaThreads) {
-    const int4 rec = bt[b];
+    const int4 rec = get_bt(b);
     int cnt = 0;
     if (mode == kModeDecode) {
       for (int i = 0; i < rec.y; ++i) cnt += cdiv(visible_limit(a.mask_mode, i, rec.y, rec.w), chunk);
@@ -103,7 +164,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
       cnt = cdiv(rec.y, a.rows_per_item);
     }
     counts[b] = cnt;
-    if (B <= kRoundRobinMaxBatch) s_counts[b] = cnt;
+    if (small) s_counts[b] = cnt;
   }
   __syncthreads();
 
@@ -111,24 +172,22 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
   const int seg = cdiv(B, kMetaThreads);
   const int b0 = tid * seg, b1 = min(b0 + seg, B);
   int local = 0;
-  for (int b = b0; b < b1; ++b) local += counts[b];
+  for (int b = b0; b < b1; ++b) local += get_count(b);
   const int incl = wave_prefix_sum(local);
   if (lane == 63) s_part[wave] = incl;
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int w = 0; w < kMetaThreads / 64; ++w) {
-      const int v = s_part[w];
-      s_part[w] = acc;
-      acc += v;
-    }
-    s_total = acc;
+  if (wave == 0) {                          // exclusive scan of the wave totals
+    const int v = lane < kMetaThreads / 64 ? s_part[lane] : 0;
+    const int inc = wave_prefix_sum(v);
+    if (lane < kMetaThreads / 64) s_part[lane] = inc - v;
+    if (lane == 63) s_total = inc;
   }
   __syncthreads();
   int run = s_part[wave] + incl - local;
   for (int b = b0; b < b1; ++b) {
     starts[b] = run;
-    run += counts[b];
+    if (small) s_starts[b] = run;
+    run += get_count(b);
   }
   const int total = min(s_total, a.max_items);
   if (tid == 0) {
@@ -147,18 +206,18 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
     int lo = 0, hi = B - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (starts[mid] <= u) lo = mid; else hi = mid - 1;
+      if (get_start(mid) <= u) lo = mid; else hi = mid - 1;
     }
     const int b = lo;
-    const int r = u - starts[b];
-    const int4 rec = bt[b];
+    const int r = u - get_start(b);
+    const int4 rec = get_bt(b);
     if (mode != kModeDecode) {
-      const int cnt = counts[b];
+      const int cnt = get_count(b);
       const int blk = cnt - 1 - r;                 // r = 0 is the last (costliest) block
       const int q0 = blk * a.rows_per_item;
       const int nrows = min(a.rows_per_item, rec.y - q0);
       int pos = u;
-      if (B <= kRoundRobinMaxBatch) {
+      if (small) {
         // round-robin over batches, each batch walked from its last block:
         // pos = sum_b' min(r, cnt_b') + #{b' < b : cnt_b' > r}
         pos = 0;
@@ -186,7 +245,10 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
 }  // namespace
 
 hipError_t launch_metadata(const KArgs& a, int mode, hipStream_t s) {
-  hipLaunchKernelGGL(metadata_kernel, dim3(1), dim3(kMetaThreads), 0, s, a, mode);
+  if (a.batch <= kRoundRobinMaxBatch)
+    hipLaunchKernelGGL(metadata_kernel<true>, dim3(1), dim3(kMetaThreads), 0, s, a, mode);
+  else
+    hipLaunchKernelGGL(metadata_kernel<false>, dim3(1), dim3(kMetaThreads), 0, s, a, mode);
   return hipGetLastError();
 }
 

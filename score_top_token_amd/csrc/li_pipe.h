@@ -8,6 +8,8 @@
 // other buffer and the loads of tile t+2 into registers overlap the compute.
 #pragma once
 
+#include <utility>
+
 #include "li_common_kernels.h"
 
 namespace li {
@@ -18,6 +20,16 @@ template <int N>
 struct IntC {
   static constexpr int value = N;
 };
+
+// f(IntC<0>()), ..., f(IntC<N-1>()) in order
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(IntC<I>()), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>());
+}
 
 // fragments of one 32-key tile
 template <int QK>
@@ -75,13 +87,16 @@ __device__ inline void pipe_schedule() {
 
 // Staging of 32-key K tiles by NT threads (global -> registers -> LDS) through
 // a ring of D register sets, so a tile's loads are issued D steps before it is
-// stored into LDS and the L2 latency hides behind D steps of compute.  Tiles at
-// or past kend are not loaded; in the tile that crosses kend the rows past it
-// are re-read from row kend-1 (their scores are masked, their content is
-// irrelevant).  Contiguous keys use one uniform tile address plus a constant
-// 32-bit lane offset.  Set indices are compile-time constants so the ring
-// stays in registers.
-template <int QK, bool PAGED, int NT, int D>
+// stored into LDS and the L2 latency hides behind D steps of compute.  In the
+// tile that crosses kend the rows past it are re-read from row kend-1 (their
+// scores are masked, their content is irrelevant).  A contiguous layout, or a paged one whose blocks hold a whole
+// number of tiles (KL_PAGED_TILE), addresses a tile by one uniform base plus a
+// constant 32-bit lane offset; other paged layouts look every key up.  Set
+// indices are compile-time constants so the ring stays in registers.
+// For fp8 keys the ring also carries the descale of the key that lane l % 32
+// reports (dsc[S]), loaded right behind the tile so that waiting for it never
+// drains the loads of later tiles.
+template <int QK, int KL, int NT, int D>
 struct PipeStage {
   static constexpr int RB = Mma<QK>::RB;
   static constexpr int NCH = RB / 16;
@@ -89,24 +104,53 @@ struct PipeStage {
   static constexpr int LOADS = (CHUNKS + NT - 1) / NT;
   static_assert(CHUNKS % NT == 0, "a tile is an exact number of chunks per thread");
   i32x4 pre[D][LOADS];
+  float dsc[D];
 
+  // kend >= 1.  A tile at or past kend re-reads key kend-1 (cache hits), so
+  // every call issues the same loads and the wait for a ring set is a static
+  // count of the loads issued after it.
   template <int S>
   __device__ inline void load(const KArgs& a, int b, int k_off, int base, int kend, int tid) {
-    if (base >= kend) return;                        // uniform: past the visible keys
+    base = base < kend ? base : kend - 1;            // uniform
     const int last = kend - 1 - base;                // last valid key of this tile
     const bool full = last >= kPipeKeys - 1;         // uniform
+    if constexpr (KL == KL_PAGED) {
 #pragma unroll
-    for (int r = 0; r < LOADS; ++r) {
-      const int id = tid + NT * r;
-      int key = id / NCH;
-      const int c = id % NCH;
-      if (!full) key = key < last ? key : last;
-      if constexpr (PAGED) {
+      for (int r = 0; r < LOADS; ++r) {
+        const int id = tid + NT * r;
+        int key = id / NCH;
+        const int c = id % NCH;
+        if (!full) key = key < last ? key : last;
         pre[S][r] = *reinterpret_cast<const i32x4*>(key_row<QK, true>(a, b, k_off, base + key) + c * 16);
+      }
+      if constexpr (QK == DT_FP8) {
+        const int key = (tid & 31) < last ? (tid & 31) : last;
+        dsc[S] = a.k_descale[key_slot<true>(a, b, k_off, base + key)];
+      }
+    } else {
+      const unsigned char* tile;
+      int64_t slot0;                                 // descale slot of the tile's first key
+      if constexpr (KL == KL_PAGED_TILE) {
+        int blk, r;
+        paged_slot(a, b, base, blk, r);
+        tile = reinterpret_cast<const unsigned char*>(a.k) + (int64_t)blk * a.k_block_stride_bytes +
+               (int64_t)r * RB;
+        slot0 = (int64_t)blk * a.block_size + r;
       } else {
-        const unsigned char* tile = reinterpret_cast<const unsigned char*>(a.k) +
-                                    ((int64_t)k_off + base) * RB;
+        tile = reinterpret_cast<const unsigned char*>(a.k) + ((int64_t)k_off + base) * RB;
+        slot0 = (int64_t)k_off + base;
+      }
+#pragma unroll
+      for (int r = 0; r < LOADS; ++r) {
+        const int id = tid + NT * r;
+        int key = id / NCH;
+        const int c = id % NCH;
+        if (!full) key = key < last ? key : last;
         pre[S][r] = *reinterpret_cast<const i32x4*>(tile + (uint32_t)(key * RB + c * 16));
+      }
+      if constexpr (QK == DT_FP8) {
+        const int key = (tid & 31) < last ? (tid & 31) : last;
+        dsc[S] = a.k_descale[slot0 + key];
       }
     }
   }

@@ -73,7 +73,7 @@ __device__ inline void write_padding(int n, int topk, int32_t* oi, float* ov) {
 // ---------------------------------------------------------------------------
 // dense kernel: 4 rows per workgroup, scores of a row kept densely in LDS
 // ---------------------------------------------------------------------------
-template <int QK, int MB, int WT, bool PAGED>
+template <int QK, int MB, int WT, int KL>
 __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
   typedef Mma<QK> M;
   typedef typename M::frag F;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
   auto emit = [&](int t, float tot) {
     const int s = t * kPipeKeys + lane;
     if (lane < 32 && s < lim) {
-      if constexpr (QK == DT_FP8) tot *= a.k_descale[key_slot<PAGED>(a, b, br.z, s)];
+      if constexpr (QK == DT_FP8) tot *= a.k_descale[key_slot<KL != KL_CONTIG>(a, b, br.z, s)];
       if (direct) {
         oi[s] = s;
         if (ov) ov[s] = tot + 0.0f;        // -0 -> +0
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
   };
 
   constexpr int D = kStageDepth;
-  PipeStage<QK, PAGED, NT, D> st;
+  PipeStage<QK, KL, NT, D> st;
   f32x16 accA[MB], accB[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
 // ---------------------------------------------------------------------------
 // streaming kernel: 4 rows per workgroup, a bounded candidate list per row
 // ---------------------------------------------------------------------------
-template <int QK, int MB, int WT, bool PAGED>
+template <int QK, int MB, int WT, int KL>
 __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_kernel(KArgs a) {
   typedef Mma<QK> M;
   typedef typename M::frag F;
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_kernel(KArgs a) {
   float thr = -__builtin_inff();           // a new key must score above this to enter
   float vmin = __builtin_inff(), vmax = -__builtin_inff();
 
-  TileStage<QK, PAGED, NT> st;
+  TileStage<QK, KL != KL_CONTIG, NT> st;
   if (ntiles > 0) {
     st.load(a, b, br.z, 0, kend, tid);
     st.store(ktile, tid);
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_kernel(KArgs a) {
       const int s = base + lane;
       const bool valid = s < lim;
       if constexpr (QK == DT_FP8) {
-        if (valid) tot *= a.k_descale[key_slot<PAGED>(a, b, br.z, s)];
+        if (valid) tot *= a.k_descale[key_slot<KL != KL_CONTIG>(a, b, br.z, s)];
       }
       tot = canon(tot);
       bool want = valid && tot > thr;
@@ -324,41 +324,44 @@ hipError_t launch_kernel(K fn, int nthreads, int grid, size_t lds, hipStream_t s
   return hipGetLastError();
 }
 
-template <int QK, int MB, int WT, bool PAGED>
+template <int QK, int MB, int WT, int KL>
 hipError_t launch_one(const KArgs& a, int mode, int grid, size_t lds, hipStream_t s) {
   if (mode == kModeDense)
-    return launch_kernel(dense_kernel<QK, MB, WT, PAGED>, kDenseWaves * 64, grid, lds, s, a);
-  return launch_kernel(stream_kernel<QK, MB, WT, PAGED>, kStreamWaves * 64, grid, lds, s, a);
+    return launch_kernel(dense_kernel<QK, MB, WT, KL>, kDenseWaves * 64, grid, lds, s, a);
+  return launch_kernel(stream_kernel<QK, MB, WT, KL>, kStreamWaves * 64, grid, lds, s, a);
 }
 
 template <int QK, int MB, int WT>
-hipError_t launch_p(const KArgs& a, int mode, bool paged, int grid, size_t lds, hipStream_t s) {
-  return paged ? launch_one<QK, MB, WT, true>(a, mode, grid, lds, s)
-               : launch_one<QK, MB, WT, false>(a, mode, grid, lds, s);
+hipError_t launch_p(const KArgs& a, int mode, int kl, int grid, size_t lds, hipStream_t s) {
+  switch (kl) {
+    case KL_CONTIG: return launch_one<QK, MB, WT, KL_CONTIG>(a, mode, grid, lds, s);
+    case KL_PAGED: return launch_one<QK, MB, WT, KL_PAGED>(a, mode, grid, lds, s);
+    default: return launch_one<QK, MB, WT, KL_PAGED_TILE>(a, mode, grid, lds, s);
+  }
 }
 
 template <int QK, int MB>
-hipError_t launch_w(const KArgs& a, int mode, int w_dtype, bool paged, int grid, size_t lds,
+hipError_t launch_w(const KArgs& a, int mode, int w_dtype, int kl, int grid, size_t lds,
                     hipStream_t s) {
-  return w_dtype == DT_FP32 ? launch_p<QK, MB, DT_FP32>(a, mode, paged, grid, lds, s)
-                            : launch_p<QK, MB, DT_BF16>(a, mode, paged, grid, lds, s);
+  return w_dtype == DT_FP32 ? launch_p<QK, MB, DT_FP32>(a, mode, kl, grid, lds, s)
+                            : launch_p<QK, MB, DT_BF16>(a, mode, kl, grid, lds, s);
 }
 
 template <int QK>
-hipError_t launch_mb(const KArgs& a, int mode, int w_dtype, int mblocks, bool paged, int grid,
+hipError_t launch_mb(const KArgs& a, int mode, int w_dtype, int mblocks, int kl, int grid,
                      size_t lds, hipStream_t s) {
-  return mblocks == 1 ? launch_w<QK, 1>(a, mode, w_dtype, paged, grid, lds, s)
-                      : launch_w<QK, 2>(a, mode, w_dtype, paged, grid, lds, s);
+  return mblocks == 1 ? launch_w<QK, 1>(a, mode, w_dtype, kl, grid, lds, s)
+                      : launch_w<QK, 2>(a, mode, w_dtype, kl, grid, lds, s);
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const KArgs& a, int mode, int qk_dtype, int w_dtype, int mblocks,
-                          bool paged, int grid, size_t lds, hipStream_t s) {
+                          int kl, int grid, size_t lds, hipStream_t s) {
   switch (qk_dtype) {
-    case DT_BF16: return launch_mb<DT_BF16>(a, mode, w_dtype, mblocks, paged, grid, lds, s);
-    case DT_FP16: return launch_mb<DT_FP16>(a, mode, w_dtype, mblocks, paged, grid, lds, s);
-    case DT_FP8: return launch_mb<DT_FP8>(a, mode, w_dtype, mblocks, paged, grid, lds, s);
+    case DT_BF16: return launch_mb<DT_BF16>(a, mode, w_dtype, mblocks, kl, grid, lds, s);
+    case DT_FP16: return launch_mb<DT_FP16>(a, mode, w_dtype, mblocks, kl, grid, lds, s);
+    case DT_FP8: return launch_mb<DT_FP8>(a, mode, w_dtype, mblocks, kl, grid, lds, s);
     default: return hipErrorInvalidValue;
   }
 }

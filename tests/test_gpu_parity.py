@@ -119,6 +119,12 @@ SMALL = {
                                          w_scale=0.125)),
     "prefill_paged": (None, 20, dict(batch=2, s1=40, n1=32, topk=64, layout_k="PA_BSND",
                                      len_lo=300, len_hi=600, block_size=16, block_pad=2)),
+    # decode rows of 32768 and 32769 visible keys: the select keeps the first in
+    # registers and streams the second from the workspace
+    "decode_rows_32k_edge": (None, 21, dict(batch=1, s1=2, s2=32769, n1=8, topk=300,
+                                            w_scale=0.35)),
+    "decode_long_rows": (None, 22, dict(batch=2, s1=1, s2=40000, n1=16, topk=512,
+                                        w_scale=0.25)),
 }
 
 
@@ -201,6 +207,67 @@ def test_paged_equals_contiguous():
     ref["name"] = "pa_eq_ref"
     ri, rv = _gpu(ref)
     assert np.array_equal(gi, ri) and np.array_equal(gv, rv)
+
+
+def _meta_items(inst):
+    """Runs li_metadata for an instance; returns (header int32[6], items [n, 4])."""
+    dev = torch.device("cuda")
+    p = binding.problem_for(inst)
+    args = {n: (inst[n].to(dev) if isinstance(inst.get(n), torch.Tensor) else None)
+            for n in ("cu_seqlens_q", "cu_seqlens_k", "seqused_k")}
+    meta = binding.lightning_indexer_metadata(p, device=dev, **args)
+    torch.cuda.synchronize()
+    m = meta.cpu().numpy()
+    hdr = m[:24].view(np.int32)
+    B = inst["batch"]
+    off = 256
+    off = -(-(off + 16 * B) // 16) * 16           # counts
+    off = -(-(off + 4 * B) // 16) * 16            # starts
+    off = -(-(off + 4 * B) // 16) * 16            # items
+    items = m[off:off + 16 * int(hdr[0])].view(np.int32).reshape(-1, 4)
+    return hdr, items
+
+
+@pytest.mark.parametrize("spec", [
+    dict(batch=64, s1=1, n1=64, topk=2048, layout_k="PA_BSND", len_lo=8192, len_hi=32768,
+         block_size=128),
+    dict(batch=7, s1=3, n1=8, topk=64, layout_k="PA_BSND", len_lo=1, len_hi=5000, block_size=32),
+    dict(batch=300, s1=2, n1=8, topk=16, layout_k="PA_BSND", len_lo=0, len_hi=3000,
+         block_size=64),
+])
+def test_decode_work_list(spec):
+    """Decode segments tile every row's visible keys exactly, start on 32-key
+    boundaries, share one length and stay within the segment budget."""
+    inst = synth.make(synth.Spec(name="wl", **spec), 5)
+    hdr, items = _meta_items(inst)
+    assert hdr[1] == 2 and hdr[3] == 0x4C494D44            # decode mode, magic
+    chunk = int(hdr[2])
+    assert chunk % 32 == 0 and chunk >= 64
+    nrows = spec["batch"] * spec["s1"]
+    target = 1024
+    while target < 2 * nrows:
+        target += 1024
+    assert len(items) <= target
+    seen = {}
+    for b, i, k0, k1 in items.tolist():
+        assert k0 % 32 == 0 and 0 < k1 - k0 <= chunk
+        seen.setdefault((b, i), []).append((k0, k1))
+    for b in range(spec["batch"]):
+        s2 = inst["seqlens_k"][b]
+        for i in range(spec["s1"]):
+            lim = max(0, min(s2, i + s2 - spec["s1"] + 1))
+            segs = sorted(seen.get((b, i), []))
+            covered = 0
+            for k0, k1 in segs:
+                assert k0 == covered
+                covered = k1
+            assert covered == lim, (b, i, segs[:3], lim)
+    # for these shapes the candidates are 32 apart: the segment length is the
+    # shortest multiple of 32 (>= 64, >= total / budget) that fits the budget
+    lims = [max(0, min(inst["seqlens_k"][b], i + inst["seqlens_k"][b] - spec["s1"] + 1))
+            for b in range(spec["batch"]) for i in range(spec["s1"])]
+    c_lo = max(64, -(-(-(-sum(lims) // target)) // 32) * 32)
+    assert chunk == c_lo or sum(-(-x // (chunk - 32)) for x in lims) > target
 
 
 # --------------------------------------------------------------------------
