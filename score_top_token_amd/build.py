@@ -30,6 +30,8 @@ def _hipcc() -> str:
 def _flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-x", "hip",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results straight into VGPRs, where the epilogue reads them
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wall", "-Wno-unused-function", "-I", os.path.join(HERE, "..", "include")]
 
 

@@ -1,5 +1,5 @@
 // Pieces shared by the score kernels: visible-key limits, key addressing,
-// operand loading, K tile staging and the ReLU / weight / head-sum epilogue.
+// operand loading and the ReLU.
 #pragma once
 
 #include "li_device.h"
@@ -117,32 +117,16 @@ __device__ inline void load_query(const KArgs& a, int64_t tok, int lane,
     }
 }
 
+// Waits for every outstanding vector-memory load (the query operands) before a
+// score loop.  Otherwise the wait-count analysis merges the loop entry (their
+// loads pending) with the back edge (loads done) and waits for them, and so for
+// every load issued after them, in each iteration.  0x0F70 encodes vmcnt(0)
+// with expcnt and lgkmcnt left at their maxima.
+__device__ inline void settle_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // max(x, 0) on the bit pattern: a negative float is a negative int32, so the
 // integer max yields +0; one VALU op with no NaN canonicalisation.
 __device__ inline float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
-
-// ReLU, per-head weight and head sum of the two 32-key column blocks of a
-// 64-key tile, acc[mb][nb].  Lanes 0-31 hold half of the heads of keys 0-31
-// (block 0) and 32-63 (block 1), lanes 32-63 the other half; after the
-// exchange lane l holds the full score of key l of the tile.  Four independent
-// chains per block keep the FMA latency off the critical path.
-template <int MB>
-__device__ inline float head_sum(const f32x16 (&acc)[MB][2], const float (&wv)[MB][16], int lane) {
-  float p0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, p1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p0[r & 3] = fmaf(wv[mb][r], relu(acc[mb][0][r]), p0[r & 3]);
-      p1[r & 3] = fmaf(wv[mb][r], relu(acc[mb][1][r]), p1[r & 3]);
-    }
-  const float s0 = (p0[0] + p0[1]) + (p0[2] + p0[3]);
-  const float s1 = (p1[0] + p1[1]) + (p1[2] + p1[3]);
-  const bool lo = lane < 32;
-  const float send = lo ? s1 : s0;
-  const float recv = __shfl_xor(send, 32);
-  return (lo ? s0 : s1) + recv;
-}
 
 template <int QK, int MB>
 __device__ inline void zero_query(typename Mma<QK>::frag (&qf)[MB][Mma<QK>::KSTEPS],
@@ -155,69 +139,5 @@ __device__ inline void zero_query(typename Mma<QK>::frag (&qf)[MB][Mma<QK>::KSTE
     for (int r = 0; r < 16; ++r) wv[mb][r] = 0.0f;
   }
 }
-
-// One 64-key score tile of a row: MFMAs over the K tile in LDS (all fragments
-// read first), then ReLU / weight / head sum.  Returns, in lane l, the score of
-// key l of the tile.
-template <int QK, int MB>
-__device__ inline float score_tile_lds(const unsigned char* tile,
-                                       const typename Mma<QK>::frag (&qf)[MB][Mma<QK>::KSTEPS],
-                                       const float (&wv)[MB][16], int lane) {
-  typedef Mma<QK> M;
-  typedef typename M::frag F;
-  F kb[2][M::KSTEPS];
-#pragma unroll
-  for (int j = 0; j < M::KSTEPS; ++j)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) kb[nb][j] = load_frag_lds<QK>(tile, nb * 32 + (lane & 31), lane, j);
-  f32x16 acc[MB][2];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    acc[mb][0] = f32x16{};
-    acc[mb][1] = f32x16{};
-  }
-#pragma unroll
-  for (int j = 0; j < M::KSTEPS; ++j)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = M::mma(qf[mb][j], kb[nb][j], acc[mb][nb]);
-  return head_sum<MB>(acc, wv, lane);
-}
-
-// Cooperative staging of one 64-key K tile: NT threads load it from global
-// memory into registers (16 bytes per chunk) and later store it into LDS in the
-// swizzled layout read by load_frag_lds.  Rows at or beyond kend are zero.
-template <int QK, bool PAGED, int NT>
-struct TileStage {
-  static constexpr int RB = Mma<QK>::RB;
-  static constexpr int NCH = RB / 16;
-  static constexpr int LOADS = kTileKeys * NCH / NT;
-  static_assert(LOADS >= 1 && kTileKeys * NCH % NT == 0, "tile split");
-  i32x4 pre[LOADS];
-
-  __device__ inline void load(const KArgs& a, int b, int k_off, int base, int kend, int tid) {
-#pragma unroll
-    for (int r = 0; r < LOADS; ++r) {
-      const int id = tid + NT * r;
-      const int key = id / NCH, c = id % NCH;
-      const int s = base + key;
-      if (s < kend) {
-        const unsigned char* row = key_row<QK, PAGED>(a, b, k_off, s);
-        pre[r] = *reinterpret_cast<const i32x4*>(row + c * 16);
-      } else {
-        pre[r] = i32x4{0, 0, 0, 0};
-      }
-    }
-  }
-  __device__ inline void store(unsigned char* tile, int tid) const {
-#pragma unroll
-    for (int r = 0; r < LOADS; ++r) {
-      const int id = tid + NT * r;
-      const int key = id / NCH, c = id % NCH;
-      *reinterpret_cast<i32x4*>(tile + lds_chunk_off<QK>(key, c)) = pre[r];
-    }
-  }
-};
 
 }  // namespace li

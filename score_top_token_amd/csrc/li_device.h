@@ -180,56 +180,4 @@ __device__ inline int wave_prefix_sum(int v) {
 
 __device__ inline void wave_sync() { __builtin_amdgcn_wave_barrier(); __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
 
-// ---------------------------------------------------------------------------
-// Wave-level exact radix select over keys[0, n) held in LDS.
-// Finds the rank-k largest key (1 <= k <= n): kth, and how many entries equal
-// to kth belong to the top k (ties_needed = k - #{key > kth}).
-// hist: 256 u32 of LDS private to this wave.
-// ---------------------------------------------------------------------------
-__device__ inline void wave_radix_select(const uint32_t* keys, int n, int k, uint32_t* hist,
-                                         uint32_t& kth, int& ties_needed) {
-  const int l = lane_id();
-  uint32_t prefix = 0, pmask = 0;
-  int rem = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int b = l; b < 256; b += 64) hist[b] = 0;
-    wave_sync();
-    for (int e = l; e < n; e += 64) {
-      const uint32_t u = keys[e];
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
-    }
-    wave_sync();
-    // lane l owns bins 4l .. 4l+3
-    const uint32_t h0 = hist[4 * l], h1 = hist[4 * l + 1], h2 = hist[4 * l + 2], h3 = hist[4 * l + 3];
-    const int s = (int)(h0 + h1 + h2 + h3);
-    const int suf = wave_suffix_sum(s);
-    const int above = suf - s;                 // entries in bins owned by higher lanes
-    const bool mine = (above < rem) && (rem <= suf);
-    int dgt = 0, gt = 0;
-    if (mine) {
-      int acc = above;
-      if (acc + (int)h3 >= rem) { dgt = 4 * l + 3; gt = acc; }
-      else {
-        acc += h3;
-        if (acc + (int)h2 >= rem) { dgt = 4 * l + 2; gt = acc; }
-        else {
-          acc += h2;
-          if (acc + (int)h1 >= rem) { dgt = 4 * l + 1; gt = acc; }
-          else { acc += h1; dgt = 4 * l; gt = acc; }
-        }
-      }
-    }
-    const uint64_t who = ballot(mine);
-    const int src = (int)__builtin_ctzll(who);
-    dgt = __shfl(dgt, src);
-    gt = __shfl(gt, src);
-    rem -= gt;
-    prefix |= ((uint32_t)dgt) << shift;
-    pmask |= 0xFFu << shift;
-    wave_sync();
-  }
-  kth = prefix;
-  ties_needed = rem;
-}
-
 }  // namespace li

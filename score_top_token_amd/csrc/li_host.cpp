@@ -88,9 +88,11 @@ li_status make_plan(const li_problem* p, Plan* pl) {
   const int B = p->batch;
   pl->mblocks = p->num_heads_q <= 32 ? 1 : 2;
   const size_t rb = (size_t)kHeadDim * elem_bytes(p->qk_dtype);     // bytes per key row
-  const size_t tile = (size_t)kTileKeys * rb;
   const int64_t dcap = (int64_t)align_up(std::max(p->max_seqlen_k, 1), 64);
-  const size_t dense_r0 = std::max(tile, (size_t)kDenseWaves * kWaveScratch);
+  // two 32-key K tiles and, for fp8, the descale slots (4 x 32 floats), or the
+  // per-wave select scratch, whichever is larger; then the score rows
+  const size_t tiles = 2 * (size_t)kPipeKeys * rb + (p->qk_dtype == LI_DT_FP8_E4M3 ? 4 * 32 * 4 : 0);
+  const size_t dense_r0 = std::max(tiles, (size_t)kDenseWaves * kWaveScratch);
   const size_t dense_lds = dense_r0 + (size_t)kDenseWaves * dcap * 4;
   int64_t items;
   if (use_decode(p)) {
@@ -111,12 +113,13 @@ li_status make_plan(const li_problem* p, Plan* pl) {
     pl->mode = kModeStream;
     pl->rows_per_item = kStreamWaves;
     items = prefill_items(p, kStreamWaves);
-    const size_t fixed = 2 * tile + (size_t)kStreamWaves * kWaveScratch;
+    // two 32-key K tiles, the descale slots, the per-wave select scratch, the lists
+    const size_t fixed = tiles + (size_t)kStreamWaves * kWaveScratch;
     const int k64 = (int)align_up(p->topk, 64);
     const int fit = (int)((kLdsBudget - fixed) / (kStreamWaves * 8) / 64 * 64);
     int cap = std::max(2 * k64, k64 + 512);
     cap = std::min(cap, fit);
-    if (cap < k64 + 64) return LI_ERR_UNSUPPORTED;
+    if (cap < k64 + 5 * kPipeKeys + 64) return LI_ERR_UNSUPPORTED;   // room for a group of tiles
     pl->cap = cap;
     pl->lds_prefill = fixed + (size_t)kStreamWaves * cap * 8;
   }

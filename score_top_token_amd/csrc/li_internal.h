@@ -12,7 +12,8 @@ namespace li {
 constexpr int kHeadDim = 128;
 constexpr int kMaxHeads = 64;
 constexpr int kMaxTopk = 2048;
-constexpr int kTileKeys = 64;           // keys per score tile (two 32-key MFMA column blocks)
+constexpr int kTileKeys = 64;           // decode: minimum keys per segment
+constexpr int kPipeKeys = 32;           // keys per K tile of the score pipelines (one MFMA column block)
 constexpr int kDenseWaves = 4;          // dense prefill: 4 query rows per workgroup, 2 workgroups / CU
 constexpr int kStreamWaves = 4;         // streaming prefill: 4 query rows per workgroup
 constexpr int kDecodeMaxRows = 4;       // decode mode: at most this many query rows per batch

@@ -6,7 +6,10 @@
 //   - a batch table {q token offset, S1_b, k token offset, S2_b},
 //   - prefill modes: one item per block of `rows_per_item` query rows, ordered so
 //     that the costliest blocks (the last rows of each sequence under right-down
-//     causal masking) are dispatched first, round-robin over the batches;
+//     causal masking) are dispatched first, round-robin over the batches with
+//     the batch order rotated every round (workgroups are dealt to the 8 XCDs by
+//     index mod 8: without the rotation a batch count that is a multiple of 8
+//     would send every block of one batch to one XCD);
 //   - decode mode: the visible keys of every query row cut into segments of one
 //     length, the shortest for which all rows together need at most
 //     kDecodeSegments segments; one item per segment.
@@ -218,13 +221,19 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
       const int nrows = min(a.rows_per_item, rec.y - q0);
       int pos = u;
       if (small) {
-        // round-robin over batches, each batch walked from its last block:
-        // pos = sum_b' min(r, cnt_b') + #{b' < b : cnt_b' > r}
-        pos = 0;
+        // round-robin over batches, each batch walked from its last block.
+        // Round r holds the n_r batches with more than r blocks; their order
+        // is rotated by r, so that a batch does not land on the same XCD
+        // (workgroup index mod 8) in every round:
+        // pos = sum_b' min(r, cnt_b') + (#{b' < b : cnt_b' > r} + r) mod n_r
+        int base = 0, idx = 0, nr = 0;
         for (int bb = 0; bb < B; ++bb) {
           const int c = s_counts[bb];
-          pos += min(r, c) + ((bb < b && c > r) ? 1 : 0);
+          base += min(r, c);
+          idx += (bb < b && c > r) ? 1 : 0;
+          nr += c > r ? 1 : 0;
         }
+        pos = base + (idx + r) % nr;
       }
       if (pos < a.max_items) items[pos] = int4{b, q0, nrows, 0};
     } else {

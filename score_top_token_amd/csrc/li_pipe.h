@@ -14,8 +14,6 @@
 
 namespace li {
 
-constexpr int kPipeKeys = 32;
-
 template <int N>
 struct IntC {
   static constexpr int value = N;
@@ -95,7 +93,8 @@ __device__ inline void pipe_schedule() {
 // indices are compile-time constants so the ring stays in registers.
 // For fp8 keys the ring also carries the descale of the key that lane l % 32
 // reports (dsc[S]), loaded right behind the tile so that waiting for it never
-// drains the loads of later tiles.
+// drains the loads of later tiles; the workgroup kernels pass it on through an
+// LDS slot per tile (kDscSlots slots of 32 floats).
 template <int QK, int KL, int NT, int D>
 struct PipeStage {
   static constexpr int RB = Mma<QK>::RB;
@@ -154,6 +153,13 @@ struct PipeStage {
       }
     }
   }
+  // fp8: the descales of the tile's 32 keys into an LDS slot (wave 0 writes)
+  template <int S>
+  __device__ inline void store_dsc(float* slot, int tid) const {
+    if constexpr (QK == DT_FP8) {
+      if (tid < 32) slot[tid] = dsc[S];
+    }
+  }
   template <int S>
   __device__ inline void store(unsigned char* tile, int tid) const {
 #pragma unroll
@@ -165,6 +171,12 @@ struct PipeStage {
   }
 };
 
-constexpr int kStageDepth = 2;   // 2 or 4 (4 exceeds the register budget at 64 heads)
+// K ring depth (tiles in flight; 2 or 4).  The dense kernel runs two
+// workgroups per CU, whose register budget leaves room for 2; the streaming
+// kernel runs one workgroup per CU and reads K from the infinity cache, so it
+// keeps 4 tiles in flight.
+constexpr int kStageDepth = 2;
+constexpr int kDscSlots = 4;      // tile t's descales live in slot t % 4 from step t-1 to t+1
+constexpr int kStreamStageDepth = 4;
 
 }  // namespace li

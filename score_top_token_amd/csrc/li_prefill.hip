@@ -79,8 +79,13 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
   typedef typename M::frag F;
   constexpr int NT = kDenseWaves * 64;
   constexpr int TILE = kPipeKeys * M::RB;
-  constexpr int R0 = 2 * TILE > kDenseWaves * kWaveScratch ? 2 * TILE : kDenseWaves * kWaveScratch;
+  // [0, R0): two K tiles and the descale slots during the score loop, the
+  // per-wave select scratch afterwards; then the score rows
+  constexpr int DSC = 2 * TILE;                      // descale slots (fp8 only)
+  constexpr int R0a = DSC + (QK == DT_FP8 ? kDscSlots * 32 * 4 : 0);
+  constexpr int R0 = R0a > kDenseWaves * kWaveScratch ? R0a : kDenseWaves * kWaveScratch;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  float* dsc_lds = reinterpret_cast<float*>(smem + DSC);
 
   const MetaHeader* hdr = reinterpret_cast<const MetaHeader*>(a.meta);
   if ((int)blockIdx.x >= hdr->n_items) return;
@@ -106,12 +111,13 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
   float wv[MB][16];
   if (has_row) load_query<QK, MB, WT>(a, tok, lane, qf, wv);
   else zero_query<QK, MB>(qf, wv);
+  settle_loads();
 
   // results of tile t: lanes 0-31 carry keys t*32 + lane
   auto emit = [&](int t, float tot) {
     const int s = t * kPipeKeys + lane;
     if (lane < 32 && s < lim) {
-      if constexpr (QK == DT_FP8) tot *= a.k_descale[key_slot<KL != KL_CONTIG>(a, b, br.z, s)];
+      if constexpr (QK == DT_FP8) tot *= dsc_lds[(t & (kDscSlots - 1)) * 32 + lane];
       if (direct) {
         oi[s] = s;
         if (ov) ov[s] = tot + 0.0f;        // -0 -> +0
@@ -137,6 +143,7 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
       st.template load<3 % D>(a, b, br.z, 3 * kPipeKeys, kend, tid);
     }
     st.template store<0>(smem, tid);
+    st.template store_dsc<0>(dsc_lds, tid);
   }
   __syncthreads();
 
@@ -145,8 +152,11 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
   // epilogue of tile t-1 from `prev`.
   auto step = [&](auto set, int t, f32x16 (&cur)[MB], const f32x16 (&prev)[MB]) {
     constexpr int S = decltype(set)::value;
-    st.template store<(S + 1) % D>(smem + ((t + 1) & 1) * TILE, tid);
+    // set S (tile t) went to LDS in the previous step: refill it first, so
+    // the wait for tile t+1 below leaves D-1 tiles in flight
     st.template load<S>(a, b, br.z, (t + D) * kPipeKeys, kend, tid);
+    st.template store<(S + 1) % D>(smem + ((t + 1) & 1) * TILE, tid);
+    st.template store_dsc<(S + 1) % D>(dsc_lds + ((t + 1) & (kDscSlots - 1)) * 32, tid);
     F kb[M::KSTEPS];
     read_tile_frags<QK>(smem + (t & 1) * TILE, lane, kb);
     mma_tile<QK, MB>(qf, kb, cur);
@@ -155,12 +165,19 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
     if (t > 0) emit(t - 1, prev_score);
     __syncthreads();
   };
-  for (int t = 0; t < ntiles; t += 4) {     // body unrolled 4x (two accumulator sets x ring)
+  // Full groups of 4 steps (two accumulator sets x ring) run unconditionally, so
+  // every step issues the same loads and the waits stay static counts; the last
+  // 0-3 tiles follow.
+  int t = 0;
+  for (; t + 4 <= ntiles; t += 4) {
     step(IntC<0>(), t, accA, accB);
-    if (t + 1 < ntiles) step(IntC<1>(), t + 1, accB, accA);
-    if (t + 2 < ntiles) step(IntC<2 % D>(), t + 2, accA, accB);
-    if (t + 3 < ntiles) step(IntC<3 % D>(), t + 3, accB, accA);
+    step(IntC<1>(), t + 1, accB, accA);
+    step(IntC<2 % D>(), t + 2, accA, accB);
+    step(IntC<3 % D>(), t + 3, accB, accA);
   }
+  if (t < ntiles) step(IntC<0>(), t, accA, accB);
+  if (t + 1 < ntiles) step(IntC<1>(), t + 1, accB, accA);
+  if (t + 2 < ntiles) step(IntC<2 % D>(), t + 2, accA, accB);
   if (ntiles > 0) {
     const int last = ntiles - 1;
     emit(last, (last & 1) ? block_score<MB>(accB, wv) : block_score<MB>(accA, wv));
@@ -188,12 +205,15 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
 // ---------------------------------------------------------------------------
 // streaming kernel: 4 rows per workgroup, a bounded candidate list per row
 // ---------------------------------------------------------------------------
+// The score loop is the dense kernel's pipeline (32-key tiles, double-buffered
+// in LDS, MFMAs of tile t interleaved with the epilogue of tile t-1); instead of
+// a full score row each wave keeps a candidate list.
 template <int QK, int MB, int WT, int KL>
 __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_kernel(KArgs a) {
   typedef Mma<QK> M;
   typedef typename M::frag F;
   constexpr int NT = kStreamWaves * 64;
-  constexpr int TILE_BYTES = kTileKeys * M::RB;
+  constexpr int TILE = kPipeKeys * M::RB;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const MetaHeader* hdr = reinterpret_cast<const MetaHeader*>(a.meta);
@@ -204,113 +224,164 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_kernel(KArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int cap = a.cap, topk = a.topk;
 
-  unsigned char* ktile = smem;
-  uint32_t* hist = reinterpret_cast<uint32_t*>(smem + 2 * TILE_BYTES + wave * kWaveScratch);
+  // LDS: two K tiles, the descale slots, the per-wave select scratch, the lists
+  constexpr int SCR = 2 * TILE + (QK == DT_FP8 ? kDscSlots * 32 * 4 : 0);
+  float* dsc_lds = reinterpret_cast<float*>(smem + 2 * TILE);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(smem + SCR + wave * kWaveScratch);
   uint32_t* scr = hist + 256;
-  float* listF = reinterpret_cast<float*>(smem + 2 * TILE_BYTES + kStreamWaves * kWaveScratch) + wave * cap;
+  float* listF = reinterpret_cast<float*>(smem + SCR + kStreamWaves * kWaveScratch) + wave * cap;
   uint32_t* listI = reinterpret_cast<uint32_t*>(listF) + kStreamWaves * cap;
 
   const bool has_row = wave < nrows;
   const int i = q0 + wave;
   const int lim = has_row ? visible_limit(a.mask_mode, i, br.y, br.w) : 0;
   const int kend = visible_limit(a.mask_mode, q0 + nrows - 1, br.y, br.w);
-  const int ntiles = (kend + kTileKeys - 1) / kTileKeys;
+  const int ntiles = (kend + kPipeKeys - 1) / kPipeKeys;
   const int64_t tok = (int64_t)br.x + i;
 
   F qf[MB][M::KSTEPS];
   float wv[MB][16];
   if (has_row) load_query<QK, MB, WT>(a, tok, lane, qf, wv);
   else zero_query<QK, MB>(qf, wv);
+  settle_loads();
 
   int count = 0;                           // candidates in this wave's list (wave-uniform)
-  float thr = -__builtin_inff();           // a new key must score above this to enter
-  float vmin = __builtin_inff(), vmax = -__builtin_inff();
+  // A key enters the list if it beats the k-th candidate: score above `thr`
+  // (keys arrive in increasing order, so a later key never wins a tie).  Until
+  // the first cut there is no k-th candidate and every key enters (incl).
+  float thr = -__builtin_inff();
+  bool incl = true;
 
-  TileStage<QK, KL != KL_CONTIG, NT> st;
-  if (ntiles > 0) {
-    st.load(a, b, br.z, 0, kend, tid);
-    st.store(ktile, tid);
-  }
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) st.load(a, b, br.z, (t + 1) * kTileKeys, kend, tid);
-    const int base = t * kTileKeys;
-    if (base < lim) {
-      float tot = score_tile_lds<QK, MB>(ktile + (t & 1) * TILE_BYTES, qf, wv, lane);
-      const int s = base + lane;
-      const bool valid = s < lim;
-      if constexpr (QK == DT_FP8) {
-        if (valid) tot *= a.k_descale[key_slot<KL != KL_CONTIG>(a, b, br.z, s)];
-      }
-      tot = canon(tot);
-      bool want = valid && tot > thr;
-      uint64_t m = ballot(want);
-      int c = __popcll(m);
-      if (c > 0) {
-        if (count + c > cap) {
-          float fb;
-          uint32_t eb;
-          wave_kth(listF, listI, count, topk, wave_min_f(vmin), wave_max_f(vmax), hist, scr, fb, eb);
-          // keep exactly k entries, in order, in place
-          int kept = 0;
-          for (int p0 = 0; p0 < count; p0 += 64) {
-            const int p = p0 + lane;
-            float f = 0.0f;
-            uint32_t e = 0;
-            bool keep = false;
-            if (p < count) {
-              f = listF[p];
-              e = listI[p];
-              keep = f > fb || (f == fb && e <= eb);
-            }
-            const uint64_t km = ballot(keep);
-            wave_sync();
-            if (keep) {
-              const int pos = kept + mbcnt(km);
-              listF[pos] = f;
-              listI[pos] = e;
-            }
-            kept += __popcll(km);
-            wave_sync();
-          }
-          count = kept < topk ? kept : topk;   // exactly topk for ordered scores
-          thr = fb;
-          vmax = wave_max_f(vmax);
-          vmin = fb;
-          want = valid && tot > thr;
-          m = ballot(want);
-          c = __popcll(m);
-        }
-        if (want) {
-          const int pos = count + mbcnt(m);
-          listF[pos] = tot;
-          listI[pos] = (uint32_t)s;
-          vmin = fminf(vmin, tot);
-          vmax = fmaxf(vmax, tot);
-        }
-        count += c;
-      }
-      wave_sync();
+  // Cuts the list back to exactly k entries (in key order, in place); the
+  // threshold rises to the k-th score.  Called between groups of tiles only,
+  // so that the insertions below never need it.
+  auto compact = [&]() __attribute__((always_inline)) {
+    float vmin = __builtin_inff(), vmax = -__builtin_inff();
+    for (int p = lane; p < count; p += 64) {
+      const float f = listF[p];
+      vmin = fminf(vmin, f);
+      vmax = fmaxf(vmax, f);
     }
-    if (t + 1 < ntiles) st.store(ktile + ((t + 1) & 1) * TILE_BYTES, tid);
-    __syncthreads();
-  }
-
-  if (!has_row) return;
-  int32_t* oi = a.out_idx + tok * topk;
-  float* ov = a.out_val ? a.out_val + tok * topk : nullptr;
-  int n = count;
-  if (count > topk) {
     float fb;
     uint32_t eb;
     wave_kth(listF, listI, count, topk, wave_min_f(vmin), wave_max_f(vmax), hist, scr, fb, eb);
-    write_kept(listF, listI, count, fb, eb, oi, ov, topk);
-    n = topk;
-  } else {
-    for (int e = lane; e < count; e += 64) {
-      oi[e] = (int32_t)listI[e];
-      if (ov) ov[e] = listF[e];
+    int kept = 0;
+    for (int p0 = 0; p0 < count; p0 += 64) {
+      const int p = p0 + lane;
+      float f = 0.0f;
+      uint32_t e = 0;
+      bool keep = false;
+      if (p < count) {
+        f = listF[p];
+        e = listI[p];
+        keep = f > fb || (f == fb && e <= eb);
+      }
+      const uint64_t km = ballot(keep);
+      wave_sync();
+      if (keep) {
+        const int pos = kept + mbcnt(km);
+        if (pos < cap) {
+          listF[pos] = f;
+          listI[pos] = e;
+        }
+      }
+      kept += __popcll(km);
+      wave_sync();
     }
+    count = kept < topk ? kept : topk;     // exactly topk for ordered scores
+    thr = fb;
+    incl = false;
+  };
+
+  // results of tile t: lanes 0-31 carry keys t*32 + lane, ds their descale.
+  // The list has room for them (count <= cap - 32).
+  auto emit = [&](int t, float tot, float ds) __attribute__((always_inline)) {
+    const int s = t * kPipeKeys + lane;
+    if constexpr (QK == DT_FP8) tot *= ds;
+    tot = canon(tot);
+    const bool want = (lane < 32) & (s < lim) & (incl ? tot >= thr : tot > thr);
+    const uint64_t m = ballot(want);
+    if (m != 0) {                          // uniform
+      const int pos = count + mbcnt(m);
+      if (want & (pos < cap)) {            // always room; bounded whatever the data
+        listF[pos] = tot;
+        listI[pos] = (uint32_t)s;
+      }
+      count += __popcll(m);
+    }
+  };
+
+  constexpr int D = kStreamStageDepth;
+  PipeStage<QK, KL, NT, D> st;
+  f32x16 accA[MB], accB[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    accA[mb] = f32x16{};
+    accB[mb] = f32x16{};
+  }
+  if (ntiles > 0) {
+    st.template load<0>(a, b, br.z, 0, kend, tid);
+    st.template load<1>(a, b, br.z, kPipeKeys, kend, tid);
+    if constexpr (D > 2) {
+      st.template load<2 % D>(a, b, br.z, 2 * kPipeKeys, kend, tid);
+      st.template load<3 % D>(a, b, br.z, 3 * kPipeKeys, kend, tid);
+    }
+    st.template store<0>(smem, tid);
+    st.template store_dsc<0>(dsc_lds, tid);
+  }
+  __syncthreads();
+
+  // Step t (ring set S = t % D): store tile t+1 into the other LDS buffer, load
+  // tile t+D into set S, MFMAs of tile t into `cur` interleaved with the
+  // epilogue of tile t-1 from `prev`, then tile t-1's candidates.
+  auto step = [&](auto set, int t, f32x16 (&cur)[MB], const f32x16 (&prev)[MB])
+                  __attribute__((always_inline)) {
+    constexpr int S = decltype(set)::value;
+    // set S (tile t) went to LDS in the previous step: refill it first, so
+    // the wait for tile t+1 below leaves D-1 tiles in flight
+    st.template load<S>(a, b, br.z, (t + D) * kPipeKeys, kend, tid);
+    st.template store<(S + 1) % D>(smem + ((t + 1) & 1) * TILE, tid);
+    st.template store_dsc<(S + 1) % D>(dsc_lds + ((t + 1) & (kDscSlots - 1)) * 32, tid);
+    F kb[M::KSTEPS];
+    read_tile_frags<QK>(smem + (t & 1) * TILE, lane, kb);
+    // tile t-1's descales (fp8), read early so the latency hides behind the MFMAs
+    const float ds = QK == DT_FP8 ? dsc_lds[((t - 1) & (kDscSlots - 1)) * 32 + (lane & 31)] : 1.0f;
+    mma_tile<QK, MB>(qf, kb, cur);
+    const float prev_score = block_score<MB>(prev, wv);
+    pipe_schedule<QK, MB>();
+    if (t > 0) emit(t - 1, prev_score, ds);
+    __syncthreads();
+  };
+  // A group of 4 steps and the final emit insert at most 5 * 32 keys: the list
+  // is cut back before a group that might not have room for them.
+  // Full groups run unconditionally (static waits, see the dense kernel); the
+  // last 0-3 tiles follow.
+  int t = 0;
+  for (; t + 4 <= ntiles; t += 4) {
+    if (count > cap - 5 * kPipeKeys) compact();   // cap >= k + 5 * 32: count > k here
+    step(IntC<0>(), t, accA, accB);
+    step(IntC<1>(), t + 1, accB, accA);
+    step(IntC<2 % D>(), t + 2, accA, accB);
+    step(IntC<3 % D>(), t + 3, accB, accA);
+  }
+  if (count > cap - 5 * kPipeKeys) compact();
+  if (t < ntiles) step(IntC<0>(), t, accA, accB);
+  if (t + 1 < ntiles) step(IntC<1>(), t + 1, accB, accA);
+  if (t + 2 < ntiles) step(IntC<2 % D>(), t + 2, accA, accB);
+  if (ntiles > 0) {
+    const int last = ntiles - 1;
+    const float ds = QK == DT_FP8 ? dsc_lds[(last & (kDscSlots - 1)) * 32 + (lane & 31)] : 1.0f;
+    emit(last, (last & 1) ? block_score<MB>(accB, wv) : block_score<MB>(accA, wv), ds);
+  }
+
+  if (!has_row) return;
+  if (count > topk) compact();             // exactly k entries, in key order
+  int32_t* oi = a.out_idx + tok * topk;
+  float* ov = a.out_val ? a.out_val + tok * topk : nullptr;
+  const int n = count < topk ? count : topk;
+  for (int e = lane; e < n; e += 64) {
+    oi[e] = (int32_t)listI[e];
+    if (ov) ov[e] = listF[e];
   }
   write_padding(n, topk, oi, ov);
 }

@@ -209,6 +209,25 @@ def test_paged_equals_contiguous():
     assert np.array_equal(gi, ri) and np.array_equal(gv, rv)
 
 
+@pytest.mark.parametrize("s2", [300, 12000])             # dense / streaming kernel
+def test_negative_infinite_scores(s2):
+    """Scores of -inf (from infinite inputs) still fill the top-k: ties broken by
+    the smaller key, values reported as -inf, no padding while keys remain."""
+    S1, N1, topk = 3, 8, 64
+    q = torch.full((1, S1, N1, 128), float("inf")).bfloat16()
+    k = torch.ones(1, s2, 1, 128).bfloat16()
+    k[0, 100:110] = -1.0                          # q.k = -inf -> ReLU 0 -> score 0
+    w = -torch.ones(1, S1, N1).bfloat16()          # every other key: -1 * ReLU(+inf) = -inf
+    inst = bsnd_inst(q, k, w, topk=topk, mask_mode=0)
+    inst["name"] = f"neg_inf_{s2}"
+    gi, gv = _gpu(inst)
+    want = sorted(list(range(100, 110)) + list(range(topk - 10)))
+    for r in range(S1):
+        assert list(gi[r]) == want
+        assert all(gv[r, want.index(e)] == 0.0 for e in range(100, 110))
+        assert np.isneginf([gv[r, j] for j, e in enumerate(want) if not 100 <= e < 110]).all()
+
+
 def _meta_items(inst):
     """Runs li_metadata for an instance; returns (header int32[6], items [n, 4])."""
     dev = torch.device("cuda")
@@ -268,6 +287,35 @@ def test_decode_work_list(spec):
             for b in range(spec["batch"]) for i in range(spec["s1"])]
     c_lo = max(64, -(-(-(-sum(lims) // target)) // 32) * 32)
     assert chunk == c_lo or sum(-(-x // (chunk - 32)) for x in lims) > target
+
+
+@pytest.mark.parametrize("spec", [
+    dict(batch=8, n1=64, topk=2048, layout_q="TND", layout_k="TND", len_lo=1024, len_hi=16384),
+    dict(batch=3, n1=8, topk=64, layout_q="TND", layout_k="TND", len_lo=10, len_hi=3000),
+    dict(batch=1, s1=4096, s2=4096, n1=64, topk=2048),
+])
+def test_prefill_work_list(spec):
+    """Prefill items cover every block of every sequence exactly once, each
+    batch's blocks come last-row-first, and no XCD (index mod 8) is fed the
+    blocks of a single batch only."""
+    inst = synth.make(synth.Spec(name="wlp", **spec), 3)
+    hdr, items = _meta_items(inst)
+    assert hdr[1] in (0, 1)                               # dense or streaming
+    rows = 4
+    want = set()
+    for b in range(spec["batch"]):
+        s1 = inst["seqlens_q"][b]
+        for q0 in range(0, s1, rows):
+            want.add((b, q0, min(rows, s1 - q0)))
+    got = [tuple(x[:3]) for x in items.tolist()]
+    assert len(got) == len(want) and set(got) == want
+    for b in range(spec["batch"]):
+        q0s = [q0 for bb, q0, _ in got if bb == b]
+        assert q0s == sorted(q0s, reverse=True)
+    if spec["batch"] > 1:
+        for b in range(spec["batch"]):
+            xcds = {u % 8 for u, (bb, _, _) in enumerate(got) if bb == b}
+            assert len(xcds) > 1
 
 
 # --------------------------------------------------------------------------
