@@ -113,8 +113,11 @@ li_status make_plan(const li_problem* p, Plan* pl) {
     pl->mode = kModeStream;
     pl->rows_per_item = kStreamWaves;
     items = prefill_items(p, kStreamWaves);
-    // two 32-key K tiles, the descale slots, the per-wave select scratch, the lists
-    const size_t fixed = tiles + (size_t)kStreamWaves * kWaveScratch;
+    // fp8: a 32-key K tile and the select scratch per wave, then the lists;
+    // otherwise two shared 32-key K tiles, the select scratch per wave, the lists
+    const size_t fixed = p->qk_dtype == LI_DT_FP8_E4M3
+                             ? (size_t)kStreamWaves * ((size_t)kPipeKeys * rb + kWaveScratch)
+                             : tiles + (size_t)kStreamWaves * kWaveScratch;
     const int k64 = (int)align_up(p->topk, 64);
     const int fit = (int)((kLdsBudget - fixed) / (kStreamWaves * 8) / 64 * 64);
     int cap = std::max(2 * k64, k64 + 512);

@@ -203,13 +203,15 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// streaming kernel: 4 rows per workgroup, a bounded candidate list per row
+// streaming kernels: 4 rows per workgroup, a bounded candidate list per row
 // ---------------------------------------------------------------------------
-// The score loop is the dense kernel's pipeline (32-key tiles, double-buffered
-// in LDS, MFMAs of tile t interleaved with the epilogue of tile t-1); instead of
-// a full score row each wave keeps a candidate list.
+// stream_shared_kernel (bf16 / fp16 keys): the dense kernel's pipeline (32-key
+// tiles shared by the workgroup, double-buffered in LDS, one barrier per tile,
+// MFMAs of tile t interleaved with the epilogue of tile t-1); instead of a full
+// score row each wave keeps a candidate list.  Sharing the tile keeps the LDS
+// traffic at one tile write per step, which 256-byte key rows need.
 template <int QK, int MB, int WT, int KL>
-__global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_kernel(KArgs a) {
+__global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_shared_kernel(KArgs a) {
   typedef Mma<QK> M;
   typedef typename M::frag F;
   constexpr int NT = kStreamWaves * 64;
@@ -293,11 +295,10 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_kernel(KArgs a) {
     incl = false;
   };
 
-  // results of tile t: lanes 0-31 carry keys t*32 + lane, ds their descale.
-  // The list has room for them (count <= cap - 32).
-  auto emit = [&](int t, float tot, float ds) __attribute__((always_inline)) {
+  // results of tile t (descaled): lanes 0-31 carry keys t*32 + lane.  The list
+  // has room for them (count <= cap - 32).
+  auto emit = [&](int t, float tot) __attribute__((always_inline)) {
     const int s = t * kPipeKeys + lane;
-    if constexpr (QK == DT_FP8) tot *= ds;
     tot = canon(tot);
     const bool want = (lane < 32) & (s < lim) & (incl ? tot >= thr : tot > thr);
     const uint64_t m = ballot(want);
@@ -333,7 +334,9 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_kernel(KArgs a) {
 
   // Step t (ring set S = t % D): store tile t+1 into the other LDS buffer, load
   // tile t+D into set S, MFMAs of tile t into `cur` interleaved with the
-  // epilogue of tile t-1 from `prev`, then tile t-1's candidates.
+  // epilogue of tile t-1 from `prev`, then tile t-2's candidates: their scores
+  // are a step old, so the insertion never waits on the epilogue's latency.
+  float pend = 0.0f;                       // descaled scores of tile t-1, not yet inserted
   auto step = [&](auto set, int t, f32x16 (&cur)[MB], const f32x16 (&prev)[MB])
                   __attribute__((always_inline)) {
     constexpr int S = decltype(set)::value;
@@ -349,11 +352,13 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_kernel(KArgs a) {
     mma_tile<QK, MB>(qf, kb, cur);
     const float prev_score = block_score<MB>(prev, wv);
     pipe_schedule<QK, MB>();
-    if (t > 0) emit(t - 1, prev_score, ds);
+    if (t > 1) emit(t - 2, pend);
+    pend = QK == DT_FP8 ? prev_score * ds : prev_score;
     __syncthreads();
   };
-  // A group of 4 steps and the final emit insert at most 5 * 32 keys: the list
-  // is cut back before a group that might not have room for them.
+  // A group of 4 steps, or the last 0-3 steps and the two final emits, insert
+  // at most 5 * 32 keys: the list is cut back before them if there might not be
+  // room.
   // Full groups run unconditionally (static waits, see the dense kernel); the
   // last 0-3 tiles follow.
   int t = 0;
@@ -371,13 +376,192 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_kernel(KArgs a) {
   if (ntiles > 0) {
     const int last = ntiles - 1;
     const float ds = QK == DT_FP8 ? dsc_lds[(last & (kDscSlots - 1)) * 32 + (lane & 31)] : 1.0f;
-    emit(last, (last & 1) ? block_score<MB>(accB, wv) : block_score<MB>(accA, wv), ds);
+    const float sc = (last & 1) ? block_score<MB>(accB, wv) : block_score<MB>(accA, wv);
+    if (last > 0) emit(last - 1, pend);
+    emit(last, QK == DT_FP8 ? sc * ds : sc);
   }
 
   if (!has_row) return;
   if (count > topk) compact();             // exactly k entries, in key order
   int32_t* oi = a.out_idx + tok * topk;
   float* ov = a.out_val ? a.out_val + tok * topk : nullptr;
+  const int n = count < topk ? count : topk;
+  for (int e = lane; e < n; e += 64) {
+    oi[e] = (int32_t)listI[e];
+    if (ov) ov[e] = listF[e];
+  }
+  write_padding(n, topk, oi, ov);
+}
+
+// stream_kernel (fp8 keys): each wave owns one row and works alone, with no
+// workgroup barrier: it streams its own visible keys through a 4-deep register
+// ring of 32-key tiles (coalesced loads), a wave-private LDS tile for the MFMA
+// operand layout, and its MFMAs interleaved with the epilogue of the previous
+// tile.  A wave whose
+// list needs cutting back, or whose row is shorter, never holds up the others;
+// the 128-byte key rows keep the four private tile copies within the LDS
+// bandwidth the MFMAs leave.
+template <int QK, int MB, int WT, int KL>
+__global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_kernel(KArgs a) {
+  typedef Mma<QK> M;
+  typedef typename M::frag F;
+  constexpr int D = kStreamStageDepth;
+  constexpr int TILE = kPipeKeys * M::RB;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const MetaHeader* hdr = reinterpret_cast<const MetaHeader*>(a.meta);
+  if ((int)blockIdx.x >= hdr->n_items) return;
+  const int4 item = reinterpret_cast<const int4*>(a.meta + a.off_items)[blockIdx.x];
+  const int b = item.x, q0 = item.y, nrows = item.z;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wave >= nrows) return;
+  const int4 br = batch_rec(a, b);
+  const int cap = a.cap, topk = a.topk;
+  const int i = q0 + wave;
+  const int lim = visible_limit(a.mask_mode, i, br.y, br.w);
+  const int64_t tok = (int64_t)br.x + i;
+  int32_t* oi = a.out_idx + tok * topk;
+  float* ov = a.out_val ? a.out_val + tok * topk : nullptr;
+
+  // LDS: per-wave K tiles, per-wave select scratch, per-wave lists
+  unsigned char* tile = smem + wave * TILE;
+  uint32_t* hist = reinterpret_cast<uint32_t*>(smem + kStreamWaves * TILE + wave * kWaveScratch);
+  uint32_t* scr = hist + 256;
+  float* listF = reinterpret_cast<float*>(smem + kStreamWaves * (TILE + kWaveScratch)) + wave * cap;
+  uint32_t* listI = reinterpret_cast<uint32_t*>(listF) + kStreamWaves * cap;
+
+  if (lim == 0) {
+    write_padding(0, topk, oi, ov);
+    return;
+  }
+  F qf[MB][M::KSTEPS];
+  float wv[MB][16];
+  load_query<QK, MB, WT>(a, tok, lane, qf, wv);
+
+  int count = 0;                           // candidates in the list (wave-uniform)
+  // A key enters the list if it beats the k-th candidate: score above `thr`
+  // (keys arrive in increasing order, so a later key never wins a tie).  Until
+  // the first cut there is no k-th candidate and every key enters (incl).
+  float thr = -__builtin_inff();
+  bool incl = true;
+
+  // Cuts the list back to exactly k entries (in key order, in place); the
+  // threshold rises to the k-th score.  Called between groups of tiles only,
+  // so that the insertions below never need it.
+  auto compact = [&]() __attribute__((always_inline)) {
+    float vmin = __builtin_inff(), vmax = -__builtin_inff();
+    for (int p = lane; p < count; p += 64) {
+      const float f = listF[p];
+      vmin = fminf(vmin, f);
+      vmax = fmaxf(vmax, f);
+    }
+    float fb;
+    uint32_t eb;
+    wave_kth(listF, listI, count, topk, wave_min_f(vmin), wave_max_f(vmax), hist, scr, fb, eb);
+    int kept = 0;
+    for (int p0 = 0; p0 < count; p0 += 64) {
+      const int p = p0 + lane;
+      float f = 0.0f;
+      uint32_t e = 0;
+      bool keep = false;
+      if (p < count) {
+        f = listF[p];
+        e = listI[p];
+        keep = f > fb || (f == fb && e <= eb);
+      }
+      const uint64_t km = ballot(keep);
+      wave_sync();
+      if (keep) {
+        const int pos = kept + mbcnt(km);
+        if (pos < cap) {
+          listF[pos] = f;
+          listI[pos] = e;
+        }
+      }
+      kept += __popcll(km);
+      wave_sync();
+    }
+    count = kept < topk ? kept : topk;     // exactly topk for ordered scores
+    thr = fb;
+    incl = false;
+  };
+
+  // results of tile t (descaled): lanes 0-31 carry keys t*32 + lane.  The list
+  // has room for them (count <= cap - 32).
+  auto emit = [&](int t, float tot) __attribute__((always_inline)) {
+    const int s = t * kPipeKeys + lane;
+    tot = canon(tot);
+    const bool want = (lane < 32) & (s < lim) & (incl ? tot >= thr : tot > thr);
+    const uint64_t m = ballot(want);
+    if (m != 0) {                          // uniform
+      const int pos = count + mbcnt(m);
+      if (want & (pos < cap)) {            // always room; bounded whatever the data
+        listF[pos] = tot;
+        listI[pos] = (uint32_t)s;
+      }
+      count += __popcll(m);
+    }
+  };
+
+  const int ntiles = (lim + kPipeKeys - 1) / kPipeKeys;
+  PipeStage<QK, KL, 64, D> st;
+  f32x16 accA[MB], accB[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    accA[mb] = f32x16{};
+    accB[mb] = f32x16{};
+  }
+  static_for<D>([&](auto set) {
+    constexpr int S = decltype(set)::value;
+    st.template load<S>(a, b, br.z, S * kPipeKeys, lim, lane);
+  });
+
+  // Step t (ring set S = t % D): tile t from set S into the wave's LDS tile,
+  // refill set S with tile t + D, MFMAs of tile t into one accumulator set
+  // interleaved with the epilogue of tile t - 1 from the other, then tile t-2's
+  // candidates: their scores are a step old, so the insertion never waits on
+  // the epilogue's latency.
+  float dcur = 1.0f;                       // descales (fp8) of tile t, then t-1
+  float pend = 0.0f;                       // descaled scores of tile t-1, not yet inserted
+  auto step = [&](auto set, int t) __attribute__((always_inline)) {
+    constexpr int S = decltype(set)::value;
+    f32x16(&cur)[MB] = (S & 1) ? accB : accA;
+    f32x16(&prev)[MB] = (S & 1) ? accA : accB;
+    st.template store<S>(tile, lane);
+    const float dprev = dcur;
+    dcur = st.dsc[S];
+    st.template load<S>(a, b, br.z, (t + D) * kPipeKeys, lim, lane);
+    wave_sync();
+    F kb[M::KSTEPS];
+    read_tile_frags<QK>(tile, lane, kb);
+    mma_tile<QK, MB>(qf, kb, cur);
+    const float prev_score = block_score<MB>(prev, wv);
+    pipe_schedule<QK, MB>();
+    if (t > 1) emit(t - 2, pend);
+    pend = QK == DT_FP8 ? prev_score * dprev : prev_score;
+    wave_sync();
+  };
+  // Full groups of D steps run unconditionally (every step issues the same
+  // loads: static waits, the ring never drains); the last tiles follow one by
+  // one.  A group, or the tail with the two final insertions, adds at most
+  // 5 * 32 keys: the list is cut back before them if there might not be room.
+  int t = 0;
+  for (; t + D <= ntiles; t += D) {
+    if (count > cap - 5 * kPipeKeys) compact();   // cap >= k + 5 * 32: count > k here
+    static_for<D>([&](auto set) { step(set, t + decltype(set)::value); });
+  }
+  if (count > cap - 5 * kPipeKeys) compact();
+  static_for<D - 1>([&](auto set) {
+    if (t + decltype(set)::value < ntiles) step(set, t + decltype(set)::value);
+  });
+  {
+    const int last = ntiles - 1;
+    const float sc = (last & 1) ? block_score<MB>(accB, wv) : block_score<MB>(accA, wv);
+    if (last > 0) emit(last - 1, pend);
+    emit(last, QK == DT_FP8 ? sc * dcur : sc);
+  }
+
+  if (count > topk) compact();             // exactly k entries, in key order
   const int n = count < topk ? count : topk;
   for (int e = lane; e < n; e += 64) {
     oi[e] = (int32_t)listI[e];
@@ -399,7 +583,10 @@ template <int QK, int MB, int WT, int KL>
 hipError_t launch_one(const KArgs& a, int mode, int grid, size_t lds, hipStream_t s) {
   if (mode == kModeDense)
     return launch_kernel(dense_kernel<QK, MB, WT, KL>, kDenseWaves * 64, grid, lds, s, a);
-  return launch_kernel(stream_kernel<QK, MB, WT, KL>, kStreamWaves * 64, grid, lds, s, a);
+  if constexpr (QK == DT_FP8)
+    return launch_kernel(stream_kernel<QK, MB, WT, KL>, kStreamWaves * 64, grid, lds, s, a);
+  else
+    return launch_kernel(stream_shared_kernel<QK, MB, WT, KL>, kStreamWaves * 64, grid, lds, s, a);
 }
 
 template <int QK, int MB, int WT>
