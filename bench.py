@@ -199,7 +199,9 @@ def main():
     # be charged to the next kernel.
     flush = None
     if args.workload in HBM_BOUND:
-        flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        # float32: the sum reads it in place (an integer sum would first widen
+        # it to int64 in a temporary, writing 2 GiB)
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
 
     for _ in range(args.warmup):
         metadata()

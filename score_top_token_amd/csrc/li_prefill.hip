@@ -70,6 +70,32 @@ __device__ inline void write_padding(int n, int topk, int32_t* oi, float* ov) {
   }
 }
 
+// Output of a wave's candidate list (key order): its top-k, streamed straight
+// from the list once the k-th element is known, then the padding.
+__device__ inline void write_list_topk(const float* listF, const uint32_t* listI, int count,
+                                       int topk, uint32_t* hist, uint32_t* scr, int32_t* oi,
+                                       float* ov) {
+  const int lane = lane_id();
+  if (count > topk) {
+    float vmin = __builtin_inff(), vmax = -__builtin_inff();
+    for (int p = lane; p < count; p += 64) {
+      const float f = listF[p];
+      vmin = fminf(vmin, f);
+      vmax = fmaxf(vmax, f);
+    }
+    float fb;
+    uint32_t eb;
+    wave_kth(listF, listI, count, topk, wave_min_f(vmin), wave_max_f(vmax), hist, scr, fb, eb);
+    write_kept(listF, listI, count, fb, eb, oi, ov, topk);
+    return;
+  }
+  for (int e = lane; e < count; e += 64) {
+    oi[e] = (int32_t)listI[e];
+    if (ov) ov[e] = listF[e];
+  }
+  write_padding(count, topk, oi, ov);
+}
+
 // ---------------------------------------------------------------------------
 // dense kernel: 4 rows per workgroup, scores of a row kept densely in LDS
 // ---------------------------------------------------------------------------
@@ -382,15 +408,9 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_shared_kernel(KAr
   }
 
   if (!has_row) return;
-  if (count > topk) compact();             // exactly k entries, in key order
   int32_t* oi = a.out_idx + tok * topk;
   float* ov = a.out_val ? a.out_val + tok * topk : nullptr;
-  const int n = count < topk ? count : topk;
-  for (int e = lane; e < n; e += 64) {
-    oi[e] = (int32_t)listI[e];
-    if (ov) ov[e] = listF[e];
-  }
-  write_padding(n, topk, oi, ov);
+  write_list_topk(listF, listI, count, topk, hist, scr, oi, ov);
 }
 
 // stream_kernel (fp8 keys): each wave owns one row and works alone, with no
@@ -561,13 +581,7 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_kernel(KArgs a) {
     emit(last, QK == DT_FP8 ? sc * dcur : sc);
   }
 
-  if (count > topk) compact();             // exactly k entries, in key order
-  const int n = count < topk ? count : topk;
-  for (int e = lane; e < n; e += 64) {
-    oi[e] = (int32_t)listI[e];
-    if (ov) ov[e] = listF[e];
-  }
-  write_padding(n, topk, oi, ov);
+  write_list_topk(listF, listI, count, topk, hist, scr, oi, ov);
 }
 
 template <class K>
