@@ -139,16 +139,20 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
   else zero_query<QK, MB>(qf, wv);
   settle_loads();
 
-  // results of tile t: lanes 0-31 carry keys t*32 + lane
+  // results of tile t (descaled): lanes 0-31 carry keys t*32 + lane.  Rows that
+  // need the select also track their minimum and maximum here.
+  float vmin = __builtin_inff(), vmax = -__builtin_inff();
   auto emit = [&](int t, float tot) {
     const int s = t * kPipeKeys + lane;
     if (lane < 32 && s < lim) {
-      if constexpr (QK == DT_FP8) tot *= dsc_lds[(t & (kDscSlots - 1)) * 32 + lane];
       if (direct) {
         oi[s] = s;
         if (ov) ov[s] = tot + 0.0f;        // -0 -> +0
       } else {
-        row[s] = canon(tot);
+        const float f = canon(tot);
+        row[s] = f;
+        vmin = fminf(vmin, f);
+        vmax = fmaxf(vmax, f);
       }
     }
   };
@@ -175,7 +179,9 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
 
   // Step t (ring set S = t % D): store tile t+1 into the other LDS buffer, load
   // tile t+D into set S, MFMAs of tile t into `cur` interleaved with the
-  // epilogue of tile t-1 from `prev`.
+  // epilogue of tile t-1 from `prev`, then tile t-2's scores are written: they
+  // are a step old, so the write never waits on the epilogue's latency.
+  float pend = 0.0f;                       // descaled scores of tile t-1, not yet written
   auto step = [&](auto set, int t, f32x16 (&cur)[MB], const f32x16 (&prev)[MB]) {
     constexpr int S = decltype(set)::value;
     // set S (tile t) went to LDS in the previous step: refill it first, so
@@ -185,10 +191,12 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
     st.template store_dsc<(S + 1) % D>(dsc_lds + ((t + 1) & (kDscSlots - 1)) * 32, tid);
     F kb[M::KSTEPS];
     read_tile_frags<QK>(smem + (t & 1) * TILE, lane, kb);
+    const float ds = QK == DT_FP8 ? dsc_lds[((t - 1) & (kDscSlots - 1)) * 32 + (lane & 31)] : 1.0f;
     mma_tile<QK, MB>(qf, kb, cur);
     const float prev_score = block_score<MB>(prev, wv);
     pipe_schedule<QK, MB>();
-    if (t > 0) emit(t - 1, prev_score);
+    if (t > 1) emit(t - 2, pend);
+    pend = QK == DT_FP8 ? prev_score * ds : prev_score;
     __syncthreads();
   };
   // Full groups of 4 steps (two accumulator sets x ring) run unconditionally, so
@@ -206,7 +214,10 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
   if (t + 2 < ntiles) step(IntC<2 % D>(), t + 2, accA, accB);
   if (ntiles > 0) {
     const int last = ntiles - 1;
-    emit(last, (last & 1) ? block_score<MB>(accB, wv) : block_score<MB>(accA, wv));
+    const float ds = QK == DT_FP8 ? dsc_lds[(last & (kDscSlots - 1)) * 32 + (lane & 31)] : 1.0f;
+    const float sc = (last & 1) ? block_score<MB>(accB, wv) : block_score<MB>(accA, wv);
+    if (last > 0) emit(last - 1, pend);
+    emit(last, QK == DT_FP8 ? sc * ds : sc);
   }
   __syncthreads();                         // the tile area becomes select scratch
   if (!has_row) return;
@@ -216,12 +227,6 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
   }
   uint32_t* hist = reinterpret_cast<uint32_t*>(smem + wave * kWaveScratch);
   uint32_t* scr = hist + 256;
-  float vmin = __builtin_inff(), vmax = -__builtin_inff();
-  for (int p = lane; p < lim; p += 64) {
-    const float f = row[p];
-    vmin = fminf(vmin, f);
-    vmax = fmaxf(vmax, f);
-  }
   float fb;
   uint32_t eb;
   wave_kth(row, nullptr, lim, topk, wave_min_f(vmin), wave_max_f(vmax), hist, scr, fb, eb);
