@@ -60,7 +60,8 @@ extern "C" {
 typedef enum {
   LI_OK = 0,
   LI_ERR_INVALID_ARGUMENT = 1,   /* a value outside the documented range, a missing pointer */
-  LI_ERR_UNSUPPORTED = 2,        /* valid for the pages but not built here (topk > 2048, cmp_ratio > 1) */
+  LI_ERR_UNSUPPORTED = 2,        /* valid for the pages but not built here (cmp_ratio > 1), or a
+                                    shape whose working set does not fit the kernels */
   LI_ERR_WORKSPACE_TOO_SMALL = 3,/* metadata or workspace buffer smaller than the size query said */
   LI_ERR_HIP = 4                 /* a HIP runtime call failed (launch error) */
 } li_status;
@@ -82,9 +83,9 @@ typedef enum {
  * Problem description (host memory, read during the call only).
  * Ranges follow the pages' constraints (lightning_indexer page, Constraints;
  * aclnnLightningIndexerV2 page, 约束说明): N of q in [1, 64], N of k = 1, head dim
- * 128, q and k of one dtype, topk in [1, 2048] (3072..8192 are accepted by the pages
- * on some hardware and give LI_ERR_UNSUPPORTED here), paged block size in [1, 1024]
- * with 32-byte-aligned blocks, and axis 0 of the paged pool may be non-contiguous.
+ * 128, q and k of one dtype, topk in [1, 2048] or one of 3072, 4096, 5120, 6144, 7168,
+ * 8192, paged block size in [1, 1024] with 32-byte-aligned blocks, and axis 0 of the
+ * paged pool may be non-contiguous.
  */
 typedef struct {
   int32_t batch;                 /* B >= 0                                                  */
@@ -95,7 +96,7 @@ typedef struct {
   int32_t num_heads_q;           /* N1 in [1, 64]                                           */
   int32_t num_heads_k;           /* N2, must be 1                                           */
   int32_t head_dim;              /* D, must be 128                                          */
-  int32_t topk;                  /* [1, 2048]                                               */
+  int32_t topk;                  /* [1, 2048], or 3072 .. 8192 in steps of 1024             */
   int32_t layout_q;              /* li_layout: BSND or TND                                  */
   int32_t layout_k;              /* li_layout: BSND, TND or PA_BSND                         */
   int32_t mask_mode;             /* 0 or 3                                                  */

@@ -87,34 +87,46 @@ __device__ inline void load_query(const KArgs& a, int64_t tok, int lane,
                               : zero_frag<QK>();
   }
   const float qd = (QK == DT_FP8) ? a.q_descale[tok] : 1.0f;
-  // accumulator rows 4g .. 4g+3 of a lane are 4 consecutive heads
+  // Accumulator rows 4g .. 4g+3 of a lane are 4 consecutive heads h0 .. h0+3
+  // (h0 a multiple of 4).  Every weight load is issued unconditionally from a
+  // clamped index and zeroed past n1 afterwards, so no branch splits them and
+  // one wait covers them all.  With n1 % 4 == 0 and an aligned w the four
+  // heads come in one vector load.
+  const bool vec = (a.n1 & 3) == 0 &&
+                   ((uintptr_t)a.w & (WT == DT_FP32 ? 15 : 7)) == 0;   // uniform
+  if (vec) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int h0 = mb * 32 + acc_row(lane, 4 * g);
-      if (h0 + 3 < a.n1 && ((tok * a.n1 + h0) & 3) == 0) {
+      for (int g = 0; g < 4; ++g) {
+        const int h0 = mb * 32 + acc_row(lane, 4 * g);
+        const bool in = h0 < a.n1;
+        const int64_t idx = tok * a.n1 + (in ? h0 : a.n1 - 4);
+        float v[4];
         if constexpr (WT == DT_FP32) {
-          const float4 v = *reinterpret_cast<const float4*>(
-              reinterpret_cast<const float*>(a.w) + tok * a.n1 + h0);
-          wv[mb][4 * g] = v.x * qd;
-          wv[mb][4 * g + 1] = v.y * qd;
-          wv[mb][4 * g + 2] = v.z * qd;
-          wv[mb][4 * g + 3] = v.w * qd;
+          const float4 x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.w) + idx);
+          v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
         } else {
-          const uint2 v = *reinterpret_cast<const uint2*>(
-              reinterpret_cast<const uint16_t*>(a.w) + tok * a.n1 + h0);
-          wv[mb][4 * g] = __uint_as_float(v.x << 16) * qd;
-          wv[mb][4 * g + 1] = __uint_as_float(v.x & 0xFFFF0000u) * qd;
-          wv[mb][4 * g + 2] = __uint_as_float(v.y << 16) * qd;
-          wv[mb][4 * g + 3] = __uint_as_float(v.y & 0xFFFF0000u) * qd;
+          const uint2 x = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.w) + idx);
+          v[0] = __uint_as_float(x.x << 16);
+          v[1] = __uint_as_float(x.x & 0xFFFF0000u);
+          v[2] = __uint_as_float(x.y << 16);
+          v[3] = __uint_as_float(x.y & 0xFFFF0000u);
         }
-      } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          wv[mb][4 * g + q] = h0 + q < a.n1 ? load_w<WT>(a.w, tok * a.n1 + h0 + q) * qd : 0.0f;
+        for (int q = 0; q < 4; ++q) wv[mb][4 * g + q] = in ? v[q] * qd : 0.0f;
       }
-    }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int h = mb * 32 + acc_row(lane, r);
+        const bool in = h < a.n1;
+        const float v = load_w<WT>(a.w, tok * a.n1 + (in ? h : a.n1 - 1));
+        wv[mb][r] = in ? v * qd : 0.0f;
+      }
+  }
 }
 
 // Waits for every outstanding vector-memory load (the query operands) before a

@@ -47,6 +47,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void split_kernel(KArgs a) {
   const int64_t tok = (int64_t)br.x + i;
   unsigned char* tile = smem + wave * TILE;
 
+  PipeStage<QK, KL, 64, D> st;
+  st.prefetch_table(a, b, k0);
   F qf[MB][M::KSTEPS];
   float wv[MB][16];
   load_query<QK, MB, WT>(a, tok, lane, qf, wv);
@@ -64,7 +66,6 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void split_kernel(KArgs a) {
 
   if (k0 >= k1) return;
   const int ntiles = (k1 - k0 + kPipeKeys - 1) / kPipeKeys;
-  PipeStage<QK, KL, 64, D> st;
   f32x16 accA[MB], accB[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -113,9 +114,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void split_kernel(KArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kSelWaves = kSelectThreads / 64;
 constexpr int kNB = kSelectBuckets;
+constexpr int kKeptSlot = 24;   // sh.misc[kKeptSlot + w]: kept elements of wave w's segment
 
 struct SelShared {
-  int misc[64];           // 0: bucket, 1: above, 2: count, 3: gathered, 4..5: fb/eb, 8..: scan
+  int misc[64];           // 0: bucket, 1: above, 2: count, 3: gathered, 4..5: fb/eb,
+                          // 6: kept counts ready, 8..23: scan, 24..39: kept per wave
   float cand_f[kSelSmall];
   uint32_t cand_e[kSelSmall];
   uint32_t hist[kNB + 64];   // + one discard bin per lane, so skipped elements never collide
@@ -204,12 +207,16 @@ constexpr int kRegSteps = 32;
 constexpr int kRegRowMax = kRegSteps * 64 * kSelWaves;   // 32768
 
 struct RegRow {
+  static constexpr bool kWaveSegments = true;   // each() visits wave w's segment in wave w
   float v[kRegSteps];
   int e0;           // this lane's element of step 0
   int steps;        // steps holding elements of this wave's segment (uniform)
+  int seg;
 
+  __device__ __forceinline__ int wave_of(uint32_t e) const { return (int)e / seg; }
   __device__ __forceinline__ void load(const float* src, int n) {
-    const int w = threadIdx.x >> 6, seg = sel_segment(n);
+    const int w = threadIdx.x >> 6;
+    seg = sel_segment(n);
     const int s1 = min(n, w * seg + seg);
     e0 = w * seg + (threadIdx.x & 63);
     steps = __builtin_amdgcn_readfirstlane(s1 > w * seg ? (s1 - w * seg + 63) / 64 : 0);
@@ -242,8 +249,11 @@ struct RegRow {
 // kSelUnroll elements are issued before any call, so their latencies overlap.
 constexpr int kSelUnroll = 8;
 struct GlobalRow {
+  static constexpr bool kWaveSegments = false;
   const float* vals;
   int n;
+
+  __device__ __forceinline__ int wave_of(uint32_t) const { return 0; }
 
   template <class F>
   __device__ __forceinline__ void each(F f) const {
@@ -336,13 +346,21 @@ struct UBucketN {
 };
 
 // gathers the (<= kSelSmall) candidates with in(f) into sh.cand_*, then wave 0
-// ranks them; the k-th element lands in sh.misc[4..5]
-template <class Row, class Pred>
-__device__ __forceinline__ void block_gather_rank(SelShared& sh, const Row& row, int r, Pred in) {
+// ranks them; the k-th element lands in sh.misc[4..5].  Every element with
+// above(f) lies above all candidates, so it is kept.  Where each wave visits
+// its own segment (RegRow) the same pass counts them per wave, the ranking wave
+// adds the kept candidates to their waves' counts, and the counts of kept
+// elements per wave land in sh.misc[kKeptSlot + w] (sh.misc[6] = 1): the
+// write needs no counting pass of its own.
+template <class Row, class Pred, class Above>
+__device__ __forceinline__ void block_gather_rank(SelShared& sh, const Row& row, int r, Pred in,
+                                                  Above above) {
   if (threadIdx.x == 0) sh.misc[3] = 0;
   __syncthreads();
+  int nab = 0;
   row.each([&](int e, bool valid, float f) {
     const bool take = valid & in(f);
+    if constexpr (Row::kWaveSegments) nab += __popcll(ballot(valid & above(f)));
     const uint64_t m = ballot(take);
     if (m != 0) {                          // uniform: one slot reservation per wave
       int base = 0;
@@ -355,6 +373,9 @@ __device__ __forceinline__ void block_gather_rank(SelShared& sh, const Row& row,
       }
     }
   });
+  if constexpr (Row::kWaveSegments) {
+    if ((threadIdx.x & 63) == 0) sh.misc[kKeptSlot + (threadIdx.x >> 6)] = nab;
+  }
   __syncthreads();
   if (threadIdx.x < 64) {
     const int m = min(sh.misc[3], kSelSmall);
@@ -367,6 +388,11 @@ __device__ __forceinline__ void block_gather_rank(SelShared& sh, const Row& row,
     if (l == 0) {
       sh.misc[4] = __float_as_int(fb);
       sh.misc[5] = (int)eb;
+    }
+    if constexpr (Row::kWaveSegments) {
+      const bool kept = (l < m) & ((cf > fb) | ((cf == fb) & (ce <= eb)));
+      if (kept) atomicAdd(&sh.misc[kKeptSlot + row.wave_of(ce)], 1);
+      if (l == 0) sh.misc[6] = 1;
     }
   }
   __syncthreads();
@@ -398,6 +424,7 @@ __device__ __forceinline__ void block_rth_equal(SelShared& sh, const Row& row, i
 template <class Row>
 __device__ __forceinline__ void block_kth(SelShared& sh, const Row& row, int k, float lo, float hi) {
   int r = k;
+  if (threadIdx.x == 0) sh.misc[6] = 0;     // published by the barriers below
   uint32_t ulo, uhi;
   if (lo < hi) {
     const FBucketN fbk(lo, hi);
@@ -411,7 +438,8 @@ __device__ __forceinline__ void block_kth(SelShared& sh, const Row& row, int k, 
     r -= above;
     __syncthreads();
     if (cnt <= kSelSmall) {
-      block_gather_rank(sh, row, r, [&](float f) { return fbk(f) == B; });
+      block_gather_rank(sh, row, r, [&](float f) { return fbk(f) == B; },
+                        [&](float f) { return fbk(f) > B; });
       return;
     }
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
@@ -448,10 +476,13 @@ __device__ __forceinline__ void block_kth(SelShared& sh, const Row& row, int k, 
     uint32_t nhi = (B == kNB - 1) ? uhi : nlo + ((1u << ubk.shift) - 1u);
     if (nhi > uhi) nhi = uhi;
     if (cnt <= kSelSmall && nlo != nhi) {
-      block_gather_rank(sh, row, r, [&](float f) {
-        const uint32_t u = f2key(f);
-        return (u >= nlo) & (u <= nhi);
-      });
+      block_gather_rank(
+          sh, row, r,
+          [&](float f) {
+            const uint32_t u = f2key(f);
+            return (u >= nlo) & (u <= nhi);
+          },
+          [&](float f) { return f2key(f) > nhi; });
       return;
     }
     ulo = nlo;
@@ -466,11 +497,15 @@ __device__ __forceinline__ void select_row(SelShared& sh, const Row& row, int to
   block_kth(sh, row, topk, lo, hi);
   const float fb = __int_as_float(sh.misc[4]);
   const uint32_t eb = (uint32_t)sh.misc[5];
+  const bool counted = sh.misc[6] != 0;
+  int kept = __builtin_amdgcn_readfirstlane(sh.misc[kKeptSlot + (threadIdx.x >> 6)]);
   __syncthreads();
-  int kept = 0;
-  row.ordered([&](int p, bool valid, float f) {
-    kept += __popcll(ballot(valid & ((f > fb) | ((f == fb) & ((uint32_t)p <= eb)))));
-  });
+  if (!counted) {
+    kept = 0;
+    row.ordered([&](int p, bool valid, float f) {
+      kept += __popcll(ballot(valid & ((f > fb) | ((f == fb) & ((uint32_t)p <= eb)))));
+    });
+  }
   int pos = block_wave_prefix(kept, sh.misc + 8, nullptr);
   const bool has_ov = ov != nullptr;
   row.ordered([&](int p, bool valid, float f) {

@@ -26,11 +26,9 @@ li_status validate_scalars(const li_problem* p) {
   if (p->num_heads_k != 1) return LI_ERR_INVALID_ARGUMENT;
   if (p->head_dim != kHeadDim) return LI_ERR_INVALID_ARGUMENT;
   if (p->topk < 1) return LI_ERR_INVALID_ARGUMENT;
-  if (p->topk > kMaxTopk) {
-    // 3072 .. 8192 in steps of 1024 are valid on the pages, not built here
-    if (p->topk <= 8192 && p->topk % 1024 == 0) return LI_ERR_UNSUPPORTED;
+  // [1, 2048], then 3072 .. 8192 in steps of 1024
+  if (p->topk > kMaxTopk && (p->topk > kMaxTopkLarge || p->topk % 1024 != 0))
     return LI_ERR_INVALID_ARGUMENT;
-  }
   if (p->layout_q != LI_LAYOUT_BSND && p->layout_q != LI_LAYOUT_TND) return LI_ERR_INVALID_ARGUMENT;
   if (p->layout_k != LI_LAYOUT_BSND && p->layout_k != LI_LAYOUT_TND &&
       p->layout_k != LI_LAYOUT_PA_BSND)
@@ -111,20 +109,27 @@ li_status make_plan(const li_problem* p, Plan* pl) {
     items = prefill_items(p, kDenseWaves);
   } else {
     pl->mode = kModeStream;
-    pl->rows_per_item = kStreamWaves;
-    items = prefill_items(p, kStreamWaves);
-    // fp8: a 32-key K tile and the select scratch per wave, then the lists;
-    // otherwise two shared 32-key K tiles, the select scratch per wave, the lists
-    const size_t fixed = p->qk_dtype == LI_DT_FP8_E4M3
-                             ? (size_t)kStreamWaves * ((size_t)kPipeKeys * rb + kWaveScratch)
-                             : tiles + (size_t)kStreamWaves * kWaveScratch;
+    // Four rows per workgroup.  fp8: a 32-key K tile and the select scratch per
+    // wave, then the lists; otherwise two shared 32-key K tiles, the select
+    // scratch per wave, the lists.  Where four lists of a large topk do not fit
+    // the workgroup holds two rows, each wave with its own K tile.
     const int k64 = (int)align_up(p->topk, 64);
-    const int fit = (int)((kLdsBudget - fixed) / (kStreamWaves * 8) / 64 * 64);
-    int cap = std::max(2 * k64, k64 + 512);
-    cap = std::min(cap, fit);
-    if (cap < k64 + 5 * kPipeKeys + 64) return LI_ERR_UNSUPPORTED;   // room for a group of tiles
+    const int need = k64 + 5 * kPipeKeys + 64;                        // room for a group of tiles
+    const size_t wave_fixed = (size_t)kPipeKeys * rb + kWaveScratch;
+    int waves = kStreamWaves;
+    size_t fixed = p->qk_dtype == LI_DT_FP8_E4M3 ? (size_t)kStreamWaves * wave_fixed
+                                                 : tiles + (size_t)kStreamWaves * kWaveScratch;
+    if ((int)((kLdsBudget - fixed) / (kStreamWaves * 8) / 64 * 64) < need) {
+      waves = kStreamWavesLarge;
+      fixed = (size_t)waves * wave_fixed;
+    }
+    const int fit = (int)((kLdsBudget - fixed) / (waves * 8) / 64 * 64);
+    const int cap = std::min(std::max(2 * k64, k64 + 512), fit);
+    if (cap < need) return LI_ERR_UNSUPPORTED;
+    pl->rows_per_item = waves;
+    items = prefill_items(p, waves);
     pl->cap = cap;
-    pl->lds_prefill = fixed + (size_t)kStreamWaves * cap * 8;
+    pl->lds_prefill = fixed + (size_t)waves * cap * 8;
   }
   if (items > INT32_MAX / 16) return LI_ERR_UNSUPPORTED;
   pl->max_items = (int32_t)items;

@@ -11,11 +11,13 @@ namespace li {
 
 constexpr int kHeadDim = 128;
 constexpr int kMaxHeads = 64;
-constexpr int kMaxTopk = 2048;
+constexpr int kMaxTopk = 2048;         // any topk up to here; above it 3072 .. 8192 in steps of 1024
+constexpr int kMaxTopkLarge = 8192;
 constexpr int kTileKeys = 64;           // decode: minimum keys per segment
 constexpr int kPipeKeys = 32;           // keys per K tile of the score pipelines (one MFMA column block)
 constexpr int kDenseWaves = 4;          // dense prefill: 4 query rows per workgroup, 2 workgroups / CU
 constexpr int kStreamWaves = 4;         // streaming prefill: 4 query rows per workgroup
+constexpr int kStreamWavesLarge = 2;    // streaming prefill, topk above 2048: 2 rows per workgroup
 constexpr int kDecodeMaxRows = 4;       // decode mode: at most this many query rows per batch
 constexpr int kDecodeWaves = 4;         // decode split kernel: waves per workgroup
 constexpr int kDecodeSegments = 1024;   // decode: key segments per pass (256 CUs x 4 waves)

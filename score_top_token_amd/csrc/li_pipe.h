@@ -104,6 +104,27 @@ struct PipeStage {
   static_assert(CHUNKS % NT == 0, "a tile is an exact number of chunks per thread");
   i32x4 pre[D][LOADS];
   float dsc[D];
+  // KL_PAGED_TILE: the physical ids of 64 consecutive logical blocks from
+  // bt_first on, lane j of each wave holding block bt_first + j.  A tile's
+  // block id is then a readlane, with no memory round trip in the step.
+  int bt_lane = 0;
+  int bt_first = -(1 << 30);
+
+  __device__ inline void bt_fill(const KArgs& a, int b, int lb) {
+    bt_first = lb;
+    int j = lb + (int)(threadIdx.x & 63);
+    j = j < a.max_blocks_per_seq ? j : a.max_blocks_per_seq - 1;
+    bt_lane = a.block_table[(int64_t)b * a.max_blocks_per_seq + j];
+  }
+  // Issues the block-table load for the tiles from key `base` on (paged keys
+  // only).  Called before the query loads, so that the first tile load waits
+  // for this one load alone.
+  __device__ inline void prefetch_table(const KArgs& a, int b, int base) {
+    if constexpr (KL == KL_PAGED_TILE) bt_fill(a, b, logical_block(a, base));
+  }
+  __device__ static inline int logical_block(const KArgs& a, int s) {
+    return a.block_shift >= 0 ? s >> a.block_shift : s / a.block_size;
+  }
 
   // kend >= 1.  A tile at or past kend re-reads key kend-1 (cache hits), so
   // every call issues the same loads and the wait for a ring set is a static
@@ -130,8 +151,15 @@ struct PipeStage {
       const unsigned char* tile;
       int64_t slot0;                                 // descale slot of the tile's first key
       if constexpr (KL == KL_PAGED_TILE) {
-        int blk, r;
-        paged_slot(a, b, base, blk, r);
+        const int lb = logical_block(a, base);
+        const int r = base - lb * a.block_size;
+        if ((unsigned)(lb - bt_first) >= 64u) {
+          // past the 64 blocks held: reload (uniform, rare) and wait for it
+          // here, so the readlane below never waits on the ring's loads
+          bt_fill(a, b, lb);
+          __builtin_amdgcn_s_waitcnt(0x0F70);
+        }
+        const int blk = __builtin_amdgcn_readlane(bt_lane, lb - bt_first);
         tile = reinterpret_cast<const unsigned char*>(a.k) + (int64_t)blk * a.k_block_stride_bytes +
                (int64_t)r * RB;
         slot0 = (int64_t)blk * a.block_size + r;

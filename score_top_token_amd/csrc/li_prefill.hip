@@ -133,6 +133,9 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
   int32_t* oi = a.out_idx + tok * topk;
   float* ov = a.out_val ? a.out_val + tok * topk : nullptr;
 
+  constexpr int D = kStageDepth;
+  PipeStage<QK, KL, NT, D> st;
+  st.prefetch_table(a, b, 0);
   F qf[MB][M::KSTEPS];
   float wv[MB][16];
   if (has_row) load_query<QK, MB, WT>(a, tok, lane, qf, wv);
@@ -157,8 +160,6 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
     }
   };
 
-  constexpr int D = kStageDepth;
-  PipeStage<QK, KL, NT, D> st;
   f32x16 accA[MB], accB[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -272,6 +273,9 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_shared_kernel(KAr
   const int ntiles = (kend + kPipeKeys - 1) / kPipeKeys;
   const int64_t tok = (int64_t)br.x + i;
 
+  constexpr int D = kStreamStageDepth;
+  PipeStage<QK, KL, NT, D> st;
+  st.prefetch_table(a, b, 0);
   F qf[MB][M::KSTEPS];
   float wv[MB][16];
   if (has_row) load_query<QK, MB, WT>(a, tok, lane, qf, wv);
@@ -343,8 +347,6 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_shared_kernel(KAr
     }
   };
 
-  constexpr int D = kStreamStageDepth;
-  PipeStage<QK, KL, NT, D> st;
   f32x16 accA[MB], accB[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -418,7 +420,8 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_shared_kernel(KAr
   write_list_topk(listF, listI, count, topk, hist, scr, oi, ov);
 }
 
-// stream_kernel (fp8 keys): each wave owns one row and works alone, with no
+// stream_kernel (fp8 keys; every key dtype when a large topk leaves room for
+// two rows per workgroup, W = 2): each wave owns one row and works alone, with no
 // workgroup barrier: it streams its own visible keys through a 4-deep register
 // ring of 32-key tiles (coalesced loads), a wave-private LDS tile for the MFMA
 // operand layout, and its MFMAs interleaved with the epilogue of the previous
@@ -426,8 +429,8 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_shared_kernel(KAr
 // list needs cutting back, or whose row is shorter, never holds up the others;
 // the 128-byte key rows keep the four private tile copies within the LDS
 // bandwidth the MFMAs leave.
-template <int QK, int MB, int WT, int KL>
-__global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_kernel(KArgs a) {
+template <int QK, int MB, int WT, int KL, int W>
+__global__ __launch_bounds__(W * 64, 1) void stream_kernel(KArgs a) {
   typedef Mma<QK> M;
   typedef typename M::frag F;
   constexpr int D = kStreamStageDepth;
@@ -450,15 +453,17 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_kernel(KArgs a) {
 
   // LDS: per-wave K tiles, per-wave select scratch, per-wave lists
   unsigned char* tile = smem + wave * TILE;
-  uint32_t* hist = reinterpret_cast<uint32_t*>(smem + kStreamWaves * TILE + wave * kWaveScratch);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(smem + W * TILE + wave * kWaveScratch);
   uint32_t* scr = hist + 256;
-  float* listF = reinterpret_cast<float*>(smem + kStreamWaves * (TILE + kWaveScratch)) + wave * cap;
-  uint32_t* listI = reinterpret_cast<uint32_t*>(listF) + kStreamWaves * cap;
+  float* listF = reinterpret_cast<float*>(smem + W * (TILE + kWaveScratch)) + wave * cap;
+  uint32_t* listI = reinterpret_cast<uint32_t*>(listF) + W * cap;
 
   if (lim == 0) {
     write_padding(0, topk, oi, ov);
     return;
   }
+  PipeStage<QK, KL, 64, D> st;
+  st.prefetch_table(a, b, 0);
   F qf[MB][M::KSTEPS];
   float wv[MB][16];
   load_query<QK, MB, WT>(a, tok, lane, qf, wv);
@@ -529,7 +534,6 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_kernel(KArgs a) {
   };
 
   const int ntiles = (lim + kPipeKeys - 1) / kPipeKeys;
-  PipeStage<QK, KL, 64, D> st;
   f32x16 accA[MB], accB[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -602,8 +606,12 @@ template <int QK, int MB, int WT, int KL>
 hipError_t launch_one(const KArgs& a, int mode, int grid, size_t lds, hipStream_t s) {
   if (mode == kModeDense)
     return launch_kernel(dense_kernel<QK, MB, WT, KL>, kDenseWaves * 64, grid, lds, s, a);
+  if (a.rows_per_item == kStreamWavesLarge)
+    return launch_kernel(stream_kernel<QK, MB, WT, KL, kStreamWavesLarge>, kStreamWavesLarge * 64,
+                         grid, lds, s, a);
   if constexpr (QK == DT_FP8)
-    return launch_kernel(stream_kernel<QK, MB, WT, KL>, kStreamWaves * 64, grid, lds, s, a);
+    return launch_kernel(stream_kernel<QK, MB, WT, KL, kStreamWaves>, kStreamWaves * 64, grid, lds,
+                         s, a);
   else
     return launch_kernel(stream_shared_kernel<QK, MB, WT, KL>, kStreamWaves * 64, grid, lds, s, a);
 }

@@ -55,7 +55,8 @@ def pa_problem(**kw):
     (dict(num_heads_q=1), OK),
     (dict(num_heads_k=2), INVALID), (dict(head_dim=64), INVALID),
     (dict(topk=0), INVALID), (dict(topk=2048), OK), (dict(topk=2049), INVALID),
-    (dict(topk=3072), UNSUPPORTED), (dict(topk=8192), UNSUPPORTED), (dict(topk=9216), INVALID),
+    (dict(topk=3072), OK), (dict(topk=8192), OK), (dict(topk=9216), INVALID),
+    (dict(topk=3000), INVALID), (dict(topk=5120), OK),
     (dict(mask_mode=1), INVALID), (dict(mask_mode=0), OK),
     (dict(layout_q=2), INVALID), (dict(layout_k=7), INVALID),
     (dict(qk_dtype=2), INVALID), (dict(qk_dtype=1), OK), (dict(qk_dtype=3), OK),
@@ -148,7 +149,7 @@ def test_forward_pointer_rules():
     assert call(prob=pa, su=F) == INVALID                 # PA needs block_table
     assert call(prob=pa, su=F, bt=F, ws=F, wsb=wb - 1) == TOO_SMALL
     assert call(prob=pa, su=F, bt=F, ws=None, wsb=wb) == INVALID
-    assert call(prob=base_problem(topk=3072)) == UNSUPPORTED
+    assert call(prob=base_problem(cmp_ratio=4)) == UNSUPPORTED
 
 
 def test_empty_problem_launches_nothing():

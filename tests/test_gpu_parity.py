@@ -125,6 +125,15 @@ SMALL = {
                                             w_scale=0.35)),
     "decode_long_rows": (None, 22, dict(batch=2, s1=1, s2=40000, n1=16, topk=512,
                                         w_scale=0.25)),
+    # topk above 2048 (3072 .. 8192 in steps of 1024): dense rows, the 4-row
+    # streaming kernel, the 2-row streaming kernel (bf16 and fp8) and decode
+    "k8192_dense": (None, 23, dict(batch=1, s1=40, s2=9000, n1=64, topk=8192, w_scale=0.125)),
+    "k3072_stream": (None, 24, dict(batch=1, s1=30, s2=12000, n1=64, topk=3072, w_scale=0.125)),
+    "k8192_stream": (None, 25, dict(batch=1, s1=20, s2=20000, n1=64, topk=8192, w_scale=0.125)),
+    "k5120_fp8_stream": (None, 26, dict(batch=1, s1=24, s2=16000, n1=64, topk=5120,
+                                        qk_dtype="fp8", w_scale=0.125)),
+    "k8192_decode": (None, 27, dict(batch=4, s1=1, n1=64, topk=8192, layout_k="PA_BSND",
+                                    len_lo=5000, len_hi=20000, block_size=128, w_scale=0.125)),
 }
 
 
