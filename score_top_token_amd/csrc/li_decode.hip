@@ -43,6 +43,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void split_kernel(KArgs a) {
   if (it >= hdr->n_items) return;
   const int4 item = reinterpret_cast<const int4*>(a.meta + a.off_items)[it];
   const int b = item.x, i = item.y, k0 = item.z, k1 = item.w;
+  if (k0 >= k1) return;                    // an empty item (padding of the work list)
   const int4 br = batch_rec(a, b);
   const int64_t tok = (int64_t)br.x + i;
   unsigned char* tile = smem + wave * TILE;
@@ -54,17 +55,22 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void split_kernel(KArgs a) {
   load_query<QK, MB, WT>(a, tok, lane, qf, wv);
   float* dst = a.ws + ((int64_t)b * a.s1max + i) * a.ws_row_stride;
 
-  // score of tile t: lanes 0-31 carry keys k0 + 32 t + lane
+  // score of tile t: lanes 0-31 carry keys k0 + 32 t + lane.  The segment's
+  // minimum and maximum stored score go to seg_mm, so that the select kernel
+  // knows each row's range before it reads the row.
+  float vmin = __builtin_inff(), vmax = -__builtin_inff();
   auto emit = [&](int t, float tot, float ds) {
     const int s = k0 + t * kPipeKeys + lane;
     if (lane < 32 && s < k1) {
       if constexpr (QK == DT_FP8) tot *= ds;
       // -0 -> +0; NaN (only from NaN inputs) -> -inf keeps the scores ordered
-      dst[s] = tot == 0.0f ? 0.0f : (tot != tot ? -__builtin_inff() : tot);
+      const float v = tot == 0.0f ? 0.0f : (tot != tot ? -__builtin_inff() : tot);
+      dst[s] = v;
+      vmin = fminf(vmin, v);
+      vmax = fmaxf(vmax, v);
     }
   };
 
-  if (k0 >= k1) return;
   const int ntiles = (k1 - k0 + kPipeKeys - 1) / kPipeKeys;
   f32x16 accA[MB], accB[MB];
 #pragma unroll
@@ -107,6 +113,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void split_kernel(KArgs a) {
   });
   const int last = ntiles - 1;
   emit(last, (last & 1) ? block_score<MB>(accB, wv) : block_score<MB>(accA, wv), dprev);
+  vmin = wave_min_f(vmin);
+  vmax = wave_max_f(vmax);
+  if (lane == 0) {
+    float* mm = a.seg_mm + ((int64_t)b * a.s1max + i) * a.seg_mm_stride * 2 + 2 * (k0 / hdr->chunk);
+    mm[0] = vmin;
+    mm[1] = vmax;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -129,26 +142,6 @@ __device__ inline uint32_t hist_slot(bool in, uint32_t bucket) {
   return in ? bucket : (uint32_t)kNB + (threadIdx.x & 63);
 }
 
-__device__ inline float block_min_f(float v, int* tmp) {
-  v = wave_min_f(v);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) tmp[w] = __float_as_int(v);
-  __syncthreads();
-  float r = __int_as_float(tmp[0]);
-  for (int x = 1; x < kSelWaves; ++x) r = fminf(r, __int_as_float(tmp[x]));
-  __syncthreads();
-  return r;
-}
-__device__ inline float block_max_f(float v, int* tmp) {
-  v = wave_max_f(v);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) tmp[w] = __float_as_int(v);
-  __syncthreads();
-  float r = __int_as_float(tmp[0]);
-  for (int x = 1; x < kSelWaves; ++x) r = fmaxf(r, __int_as_float(tmp[x]));
-  __syncthreads();
-  return r;
-}
 __device__ inline uint32_t block_min_u(uint32_t v, int* tmp) {
   v = wave_min_u(v);
   if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = (int)v;
@@ -547,25 +540,24 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(KArgs a) {
     }
     return;
   }
+  // the row's range from its segments' (min, max), reduced by every wave on
+  // its own (no barrier), while the row's own loads are in flight
+  const int chunk = reinterpret_cast<const MetaHeader*>(a.meta)->chunk;
+  const int nseg = (lim + chunk - 1) / chunk;
+  const float* mm = a.seg_mm + (int64_t)r * a.seg_mm_stride * 2;
   float mn = __builtin_inff(), mx = -__builtin_inff();
+  for (int j = tid & 63; j < nseg; j += 64) {
+    mn = fminf(mn, mm[2 * j]);
+    mx = fmaxf(mx, mm[2 * j + 1]);
+  }
+  const float lo = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_min_f(mn))));
+  const float hi = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max_f(mx))));
   if (lim <= kRegRowMax) {
     RegRow row;
     row.load(src, lim);
-    row.each([&](int, bool, float f) {   // padding NaNs are ignored by fminf / fmaxf
-      mn = fminf(mn, f);
-      mx = fmaxf(mx, f);
-    });
-    const float lo = block_min_f(mn, sh.misc + 8);
-    const float hi = block_max_f(mx, sh.misc + 8);
     select_row(sh, row, topk, lo, hi, oi, ov);
   } else {
     const GlobalRow row{src, lim};
-    row.each([&](int, bool valid, float f) {
-      mn = valid ? fminf(mn, f) : mn;
-      mx = valid ? fmaxf(mx, f) : mx;
-    });
-    const float lo = block_min_f(mn, sh.misc + 8);
-    const float hi = block_max_f(mx, sh.misc + 8);
     select_row(sh, row, topk, lo, hi, oi, ov);
   }
 }

@@ -96,10 +96,13 @@ li_status make_plan(const li_problem* p, Plan* pl) {
   if (use_decode(p)) {
     pl->mode = kModeDecode;
     pl->chunk = kTileKeys;                // minimum segment; the device picks the real one
-    // segments <= target + rows, target <= kDecodeSegments + 2 * rows
-    items = 3 * (int64_t)B * p->max_seqlen_q + kDecodeSegments;
+    // segments <= target + rows, target <= kDecodeSegments + 2 * rows; padded
+    // to whole rounds of 8 workgroups
+    items = align_up(3 * (int64_t)B * p->max_seqlen_q + kDecodeSegments, 8 * kDecodeWaves);
     pl->ws_row_stride = (int64_t)align_up(p->max_seqlen_k, 64);
-    pl->ws_bytes = (size_t)B * p->max_seqlen_q * pl->ws_row_stride * 4;
+    // then the (min, max) of each segment (at least kTileKeys keys long)
+    pl->seg_mm_stride = (int32_t)cdiv64(std::max(p->max_seqlen_k, 1), kTileKeys);
+    pl->ws_bytes = (size_t)B * p->max_seqlen_q * ((size_t)pl->ws_row_stride * 4 + (size_t)pl->seg_mm_stride * 8);
     pl->lds_select = select_shared_bytes();
   } else if (dense_lds <= kLdsBudget) {
     pl->mode = kModeDense;
@@ -180,6 +183,7 @@ KArgs base_args(const li_problem* p, const Plan& pl, void* metadata) {
   a.chunk = pl.chunk;
   a.max_items = pl.max_items;
   a.ws_row_stride = pl.ws_row_stride;
+  a.seg_mm_stride = pl.seg_mm_stride;
   a.off_batch = (int32_t)pl.off_batch;
   a.off_counts = (int32_t)pl.off_counts;
   a.off_starts = (int32_t)pl.off_starts;
@@ -260,6 +264,8 @@ li_status li_forward(const li_problem* p, const void* q, const void* k, const vo
   a.cu_k = cu_seqlens_k;
   a.seqused_k = seqused_k;
   a.ws = static_cast<float*>(workspace);
+  if (pl.mode == kModeDecode)
+    a.seg_mm = a.ws + (size_t)p->batch * p->max_seqlen_q * pl.ws_row_stride;
   a.out_idx = sparse_indices;
   a.out_val = sparse_values;
   const int qk = p->qk_dtype, wt = p->w_dtype;

@@ -62,6 +62,7 @@ struct Plan {
   size_t off_batch, off_counts, off_starts, off_items;
   size_t ws_bytes;
   int64_t ws_row_stride;  // decode: fp32 slots per (batch, row) score row
+  int32_t seg_mm_stride;  // decode: segment (min, max) pairs per row
 };
 
 // Kernel argument block (passed by value).
@@ -77,10 +78,12 @@ struct KArgs {
   const int32_t* seqused_k;
   unsigned char* meta;      // metadata base
   float* ws;                // decode: dense score rows
+  float* seg_mm;            // decode: (min, max) score of each segment, seg_mm_stride pairs per row
   int32_t* out_idx;
   float* out_val;
   int64_t k_block_stride_bytes;   // bytes between paged blocks
   int64_t ws_row_stride;
+  int32_t seg_mm_stride;
   int32_t batch, s1max, s2max;
   int32_t n1, topk;
   int32_t layout_q, layout_k, mask_mode;

@@ -12,7 +12,12 @@
 //     would send every block of one batch to one XCD);
 //   - decode mode: the visible keys of every query row cut into segments of one
 //     length, the shortest for which all rows together need at most
-//     kDecodeSegments segments; one item per segment.
+//     kDecodeSegments segments; one item per segment.  The split kernel runs
+//     kDecodeWaves items per workgroup, and workgroup w lands on XCD w mod 8,
+//     whose share of HBM bandwidth bounds it: the full-length segments are dealt
+//     round-robin over the XCDs, then the shorter last segments of the rows, and
+//     the list is padded with empty items to whole rounds (batches up to
+//     kRoundRobinMaxBatch; larger ones keep row order).
 // The result depends only on the lengths (deterministic) and is produced on the
 // device, so the call never synchronises with the host.
 #include "li_pipe.h"
@@ -46,6 +51,8 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
   __shared__ int s_starts[kRoundRobinMaxBatch];
   __shared__ int4 s_bt[kRoundRobinMaxBatch];
   __shared__ int s_part[kMetaThreads / 64];
+  __shared__ int s_pstart[kRoundRobinMaxBatch];   // decode: partial segments before batch b
+  __shared__ int s_npart;                          // decode: all partial segments
   __shared__ unsigned long long s_cand[kChunkCands], s_tot, s_nrows;
   __shared__ int s_total, s_chunk;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -193,8 +200,37 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
     run += get_count(b);
   }
   const int total = min(s_total, a.max_items);
+  // decode, small batches: segments shorter than `chunk` (at most one per row,
+  // the last) counted per batch and scanned by wave 0, four batches per lane
+  constexpr int kXcdRound = 8 * kDecodeWaves;
+  const bool xcd_deal = small && mode == kModeDecode;
+  int n_slots = total;
+  if (xcd_deal) {
+    if (wave == 0) {
+      int pc[4], sum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int b = 4 * lane + q;
+        pc[q] = 0;
+        if (b < B) {
+          const int4 rec = get_bt(b);
+          for (int i = 0; i < rec.y; ++i)
+            pc[q] += (visible_limit(a.mask_mode, i, rec.y, rec.w) % chunk) != 0;
+        }
+        sum += pc[q];
+      }
+      int run = wave_prefix_sum(sum) - sum;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (4 * lane + q < B) s_pstart[4 * lane + q] = run;
+        run += pc[q];
+      }
+      if (lane == 63) s_npart = run;
+    }
+    n_slots = min((total + kXcdRound - 1) / kXcdRound * kXcdRound, a.max_items);
+  }
   if (tid == 0) {
-    hdr->n_items = total;
+    hdr->n_items = n_slots;
     hdr->mode = mode;
     hdr->chunk = chunk;
     hdr->magic = kMetaMagic;
@@ -237,16 +273,34 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
       }
       if (pos < a.max_items) items[pos] = int4{b, q0, nrows, 0};
     } else {
-      int rest = r, i = 0, lim = 0;
+      int rest = r, i = 0, lim = 0, part = 0;
       for (; i < rec.y; ++i) {
         lim = visible_limit(a.mask_mode, i, rec.y, rec.w);
         const int nch = cdiv(lim, chunk);
         if (rest < nch) break;
         rest -= nch;
+        part += (lim % chunk) != 0;
       }
       const int k0 = rest * chunk;
       const int k1 = min(k0 + chunk, lim);
-      items[u] = int4{b, i, k0, k1};
+      int pos = u;
+      if (xcd_deal) {
+        // rank j among the full segments (row order), or after all of them
+        // among the partial ones; the j-th goes to XCD j mod 8
+        const int pbefore = s_pstart[b] + part;
+        const int j = k1 - k0 == chunk ? u - pbefore : total - s_npart + pbefore;
+        const int k = j >> 3;
+        pos = ((k / kDecodeWaves) * 8 + (j & 7)) * kDecodeWaves + k % kDecodeWaves;
+      }
+      if (pos < a.max_items) items[pos] = int4{b, i, k0, k1};
+    }
+  }
+  // empty items in the slots no segment was dealt to
+  if (xcd_deal) {
+    for (int s = tid; s < n_slots; s += kMetaThreads) {
+      const int k = (s / kDecodeWaves / 8) * kDecodeWaves + s % kDecodeWaves;
+      const int j = k * 8 + (s / kDecodeWaves) % 8;
+      if (j >= total) items[s] = int4{0, 0, 0, 0};
     }
   }
 }

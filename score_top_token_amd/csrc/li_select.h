@@ -98,9 +98,10 @@ __device__ inline void wave_find_bucket(const uint32_t* hist, int r, int& bkt, i
 __device__ inline void wave_rank_small(float f, uint32_t e, int m, int r, float& fb, uint32_t& eb) {
   const int l = lane_id();
   int rank = 0;
+  m = __builtin_amdgcn_readfirstlane(m);       // uniform: the loop broadcasts by readlane
   for (int j = 0; j < m; ++j) {
-    const float fj = __shfl(f, j);
-    const uint32_t ej = (uint32_t)__shfl((int)e, j);
+    const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j));
+    const uint32_t ej = (uint32_t)__builtin_amdgcn_readlane((int)e, j);
     rank += (fj > f || (fj == f && ej < e)) ? 1 : 0;
   }
   const bool hit = l < m && rank == r - 1;

@@ -275,11 +275,23 @@ def test_decode_work_list(spec):
     target = 1024
     while target < 2 * nrows:
         target += 1024
-    assert len(items) <= target
+    real = items[items[:, 3] > items[:, 2]]
+    assert len(real) <= target
+    assert (items[items[:, 3] <= items[:, 2]] == 0).all()       # padding items are empty
     seen = {}
-    for b, i, k0, k1 in items.tolist():
+    for b, i, k0, k1 in real.tolist():
         assert k0 % 32 == 0 and 0 < k1 - k0 <= chunk
         seen.setdefault((b, i), []).append((k0, k1))
+    if spec["batch"] <= 256:
+        # whole rounds of 8 workgroups x 4 items; workgroup w runs on XCD w % 8:
+        # every XCD gets the same number of full segments and of short ones, +-1
+        assert len(items) % 32 == 0
+        xcd = (np.arange(len(items)) // 4) % 8
+        full = items[:, 3] - items[:, 2] == chunk
+        short = (items[:, 3] > items[:, 2]) & ~full
+        for m in (full, short):
+            per = np.bincount(xcd[m], minlength=8)
+            assert per.max() - per.min() <= 1, per
     for b in range(spec["batch"]):
         s2 = inst["seqlens_k"][b]
         for i in range(spec["s1"]):
