@@ -34,6 +34,7 @@ class _Problem(ctypes.Structure):
         ("mask_mode", ctypes.c_int32), ("qk_dtype", ctypes.c_int32),
         ("w_dtype", ctypes.c_int32), ("block_size", ctypes.c_int32),
         ("max_blocks_per_seq", ctypes.c_int32), ("k_block_stride", ctypes.c_int64),
+        ("cmp_ratio", ctypes.c_int32),
     ]
 
 
@@ -43,6 +44,7 @@ class _Inputs(ctypes.Structure):
         ("q_descale", ctypes.c_void_p), ("k_descale", ctypes.c_void_p),
         ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
         ("seqused_k", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+        ("cmp_residual_k", ctypes.c_void_p), ("output_idx_offset", ctypes.c_void_p),
     ]
 
 
@@ -132,10 +134,12 @@ class Bound:
             layout_q=_LAYOUT[inst["layout_q"]], layout_k=_LAYOUT[inst["layout_k"]],
             mask_mode=inst["mask_mode"], qk_dtype=_DTYPE[inst["qk_dtype"]],
             w_dtype=_DTYPE[inst["w_dtype"]], block_size=inst.get("block_size", 0) or 0,
-            max_blocks_per_seq=inst.get("max_blocks_per_seq", 0) or 0, k_block_stride=kstride)
+            max_blocks_per_seq=inst.get("max_blocks_per_seq", 0) or 0, k_block_stride=kstride,
+            cmp_ratio=inst.get("cmp_ratio", 1) or 1)
         self._keep = [inst.get(n) for n in ("q", "k", "w", "q_descale", "k_descale",
                                             "cu_seqlens_q", "cu_seqlens_k", "seqused_k",
-                                            "block_table")]
+                                            "block_table", "cmp_residual_k",
+                                            "output_idx_offset")]
         for t in self._keep:
             if t is not None:
                 assert t.device.type == "cpu"
@@ -143,7 +147,9 @@ class Bound:
             q=_ptr(q), k=_ptr(k), w=_ptr(w), q_descale=_ptr(inst.get("q_descale")),
             k_descale=_ptr(inst.get("k_descale")), cu_seqlens_q=_ptr(inst.get("cu_seqlens_q")),
             cu_seqlens_k=_ptr(inst.get("cu_seqlens_k")), seqused_k=_ptr(inst.get("seqused_k")),
-            block_table=_ptr(inst.get("block_table")))
+            block_table=_ptr(inst.get("block_table")),
+            cmp_residual_k=_ptr(inst.get("cmp_residual_k")),
+            output_idx_offset=_ptr(inst.get("output_idx_offset")))
 
     @property
     def num_rows(self) -> int:

@@ -13,12 +13,20 @@
  *      rightDownCausal, the lower triangle anchored at the bottom-right corner
  *      (npu_lightning_indexer_pto page, sparse_mode), read as
  *      s <= i + S2_b - S1_b, diagonal included ("the current token and all
- *      preceding tokens", lightning_indexer page, Function step 2);
+ *      preceding tokens", lightning_indexer page, Function step 2).
+ *      Compressed keys (cmp_ratio r > 1, lightning_indexer page, parameters and
+ *      Example): key j stands for the r original positions j*r .. j*r + r - 1,
+ *      the batch has S2_b*r + cmp_residual_k[b] original keys (the residual ones
+ *      trail, not yet compressed), local row i is original position
+ *      i + S2_b*r + res_b - S1_b, and it sees key j when the whole block lies at
+ *      or before that position (a reading: the pages give the shapes only);
  *   3. score I = sum_h w[h] * max(0, sum_d q[h,d] * k[s,d]) in fp64 (the formula of
  *      the npu_lightning_indexer_pto page; steps 1-3 of the lightning_indexer page);
  *      fp8 codes are multiplied by their per-token descale;
  *   4. rank visible keys by (I descending, s ascending), keep n = min(topk, |V|),
- *      pad the rest with -1 / -inf (lightning_indexer page, Constraints).
+ *      pad the rest with -1 / -inf (lightning_indexer page, Constraints); with
+ *      output_idx_offset each kept index of batch b is written plus offset[b]
+ *      (aclnnLightningIndexerV2 page, 约束说明: a positive index offset).
  */
 #include "li_oracle.h"
 
@@ -131,6 +139,16 @@ int lio_row_coords(const lio_problem* p, const lio_inputs* in, int64_t row, int*
 int lio_visible_count(const lio_problem* p, const lio_inputs* in, int b, int i) {
   int S1 = seqlen_q(p, in, b), S2 = seqlen_k(p, in, b);
   if (p->mask_mode == 0) return S2;
+  if (p->cmp_ratio > 1) {
+    /* count the compressed keys whose whole block of original positions ends
+     * at or before the row's original position */
+    long long r = p->cmp_ratio;
+    long long pos = (long long)i + (long long)S2 * r + in->cmp_residual_k[b] - S1;
+    int n = 0;
+    for (int j = 0; j < S2; ++j)
+      if ((long long)j * r + r - 1 <= pos) ++n;
+    return n;
+  }
   long long last = (long long)i + S2 - S1;     /* largest visible key */
   if (last < 0) return 0;
   if (last >= S2) return S2;
@@ -209,9 +227,10 @@ static void one_row(const lio_problem* p, const lio_inputs* in, int64_t row, int
     qsort(c, (size_t)nvis, sizeof(cand), cand_cmp);
   }
   int n = nvis < p->topk ? nvis : p->topk;
+  int32_t off = in->output_idx_offset && nvis > 0 ? in->output_idx_offset[b] : 0;
   for (int j = 0; j < p->topk; ++j) {
     if (j < n) {
-      oi[j] = c[j].key;
+      oi[j] = c[j].key + off;
       ov[j] = (float)c[j].score + 0.0f;              /* one RNE rounding; -0 -> +0 */
     } else {
       oi[j] = -1;
@@ -255,6 +274,7 @@ int lio_forward(const lio_problem* p, const lio_inputs* in, const int64_t* rows,
   if (p->layout_k == LIO_PA_BSND && (!in->seqused_k || !in->block_table || p->block_size <= 0))
     return -1;
   if (p->qk_dtype == LIO_E4M3 && (!in->q_descale || !in->k_descale)) return -1;
+  if (p->cmp_ratio > 1 && p->mask_mode == 3 && !in->cmp_residual_k) return -1;
   if (!rows) nrows = lio_num_rows(p, in);
   if (nthreads <= 0) nthreads = 1;
   if (nthreads > 256) nthreads = 256;

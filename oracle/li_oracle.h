@@ -19,7 +19,8 @@
  * Scores are computed in fp64 with a fixed order (h ascending, d ascending),
  * ranked by (score descending, key index ascending), and the value written is
  * the fp64 score rounded once to fp32 (round to nearest even), with -0 turned
- * into +0.  Indices are sequence-local logical key positions.
+ * into +0.  Indices are sequence-local logical key positions (compressed-key
+ * positions when cmp_ratio > 1), plus the batch's output index offset if given.
  */
 #ifndef LI_ORACLE_H
 #define LI_ORACLE_H
@@ -54,6 +55,7 @@ typedef struct {
   int32_t block_size;        /* PA only */
   int32_t max_blocks_per_seq;/* PA only: columns of block_table */
   int64_t k_block_stride;    /* PA only: elements between consecutive pool blocks */
+  int32_t cmp_ratio;         /* original key positions per key (<= 1: no compression) */
 } lio_problem;
 
 typedef struct {
@@ -66,6 +68,8 @@ typedef struct {
   const int32_t* cu_seqlens_k;  /* TND k: B inclusive prefix sums */
   const int32_t* seqused_k;     /* PA: keys per batch */
   const int32_t* block_table;   /* PA: [B, max_blocks_per_seq] */
+  const int32_t* cmp_residual_k;     /* cmp_ratio > 1 with mask 3: [B], each in [0, cmp_ratio) */
+  const int32_t* output_idx_offset;  /* NULL or [B]: added to every kept index of the batch */
 } lio_inputs;
 
 /* Number of query rows (B*S1 for BSND, T1 for TND). */

@@ -14,7 +14,10 @@ preceding batches").
 
 Draw order for a seed (torch.Generator on the CPU, fp32, then a round-to-
 nearest-even cast): sequence lengths (TND / PA only), q, k, w, the block
-permutation (PA only).  fp8 data is quantized per token from fp32 N(0,1) draws:
+permutation (PA only), then the per-batch compression residuals (cmp_ratio > 1
+with mask 3) and output index offsets (idx_offset_max > 0).  Compressed keys
+are drawn like any other keys: the generator does not compress anything, k
+simply holds S2_b keys that each stand for cmp_ratio original positions.  fp8 data is quantized per token from fp32 N(0,1) draws:
 descale = amax/448 over the token's values, code = e4m3fn(x/descale) after a
 clamp to +-448.
 """
@@ -62,6 +65,13 @@ class Spec:
     # chunked prefill / decode: key count S2 > S1 (right-down causal aligns the
     # last query with the last key).
     fixed_lengths: Optional[list] = None    # overrides the drawn lengths
+    # compressed keys: each key stands for cmp_ratio original positions; with
+    # mask 3 every batch draws a residual in [0, cmp_ratio) (trailing original
+    # keys not yet compressed), unless fixed_residuals gives them
+    cmp_ratio: int = 1
+    fixed_residuals: Optional[list] = None
+    # output index offsets: per batch, drawn in [1, idx_offset_max] when > 0
+    idx_offset_max: int = 0
 
 
 PRESETS = {
@@ -133,6 +143,7 @@ def make(spec: Spec | str, seed: int = 0) -> dict:
                w_dtype=spec.w_dtype, block_size=0, num_blocks=0, max_blocks_per_seq=0,
                total_q=0, total_k=0, cu_seqlens_q=None, cu_seqlens_k=None,
                seqused_k=None, block_table=None, q_descale=None, k_descale=None,
+               cmp_ratio=spec.cmp_ratio, cmp_residual_k=None, output_idx_offset=None,
                name=spec.name, seed=int(seed))
 
     # ---- lengths ---------------------------------------------------------
@@ -213,6 +224,16 @@ def make(spec: Spec | str, seed: int = 0) -> dict:
             used = -(-lk[b] // bs)
             bt[b, used:] = -1
         out["block_table"] = bt.contiguous()
+
+    if spec.cmp_ratio > 1 and spec.mask_mode == 3:
+        if spec.fixed_residuals is not None:
+            res = torch.tensor([int(v) for v in spec.fixed_residuals], dtype=torch.int32)
+        else:
+            res = torch.randint(0, spec.cmp_ratio, (B,), generator=g).to(torch.int32)
+        out["cmp_residual_k"] = res.contiguous()
+    if spec.idx_offset_max > 0:
+        out["output_idx_offset"] = torch.randint(1, spec.idx_offset_max + 1, (B,),
+                                                 generator=g).to(torch.int32).contiguous()
     return out
 
 

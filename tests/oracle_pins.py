@@ -12,7 +12,10 @@ something the pages or the mathematics fix:
     ties going to the smaller index) and the all-zero-score case;
   - layout equivalences: paged K with a random block table and padded pool,
     TND packing, fp8 codes with unit descales, fp16 codes, fp32 weights;
-  - exact power-of-two scaling laws of w and of the fp8 descales.
+  - exact power-of-two scaling laws of w and of the fp8 descales;
+  - compressed keys (cmp_ratio): visible counts against a walk over the original
+    sequence for the pages' example shapes and a closed form, scores unchanged by
+    compression; output index offsets.
 tests/test_oracle_pins.py runs them on the real oracle; tests/test_oracle_mutants.py
 runs them on copies of the oracle with planted mistakes and requires each mistake
 to be caught.
@@ -370,6 +373,111 @@ def pin_pages_example_shape():
         i = r % S1
         vis = min(max(i + S2 - S1 + 1, 0), S2)
         assert valid_prefix_len(idx[r]) == min(topk, vis)
+
+
+def _simulated_compressed_counts(S1, S2_orig, r):
+    """Visible compressed keys per query row, by walking the original sequence:
+    a compressed key exists once all r of its original positions have passed;
+    the trailing S2_orig % r positions never complete a key.  The S1 query rows
+    are the last S1 original positions (right-down alignment)."""
+    done, counts = 0, []
+    for t in range(S2_orig):
+        if (t + 1) % r == 0:
+            done += 1
+        if t >= S2_orig - S1:
+            counts.append(done)
+    return counts
+
+
+def pin_pages_example_compressed():
+    """The same example with its compression: 130 original keys, cmp_ratio 4 ->
+    32 keys with residual 2; row i sees the keys whose 4 original positions all
+    lie at or before its own original position."""
+    import json
+    import os
+    here = os.path.dirname(os.path.abspath(__file__))
+    with open(os.path.join(here, "golden", "pages_example_compressed.json")) as f:
+        ex = json.load(f)
+    B, S1, S2o, r, N1, D, topk = (ex[n] for n in ("B", "S1", "S2_original", "cmp_ratio", "N1",
+                                                  "D", "topk"))
+    S2, res = S2o // r, S2o % r
+    g = torch.Generator().manual_seed(1)
+    q = torch.randn(B, S1, N1, D, generator=g).half()
+    k = torch.randn(B, S2, 1, D, generator=g).half()
+    w = torch.randn(B, S1, N1, generator=g)
+    inst = bsnd_inst(q, k, w, topk=topk, mask_mode=ex["mask_mode"], qk_dtype="fp16",
+                     w_dtype="fp32")
+    inst["cmp_ratio"] = r
+    inst["cmp_residual_k"] = torch.full((B,), res, dtype=torch.int32)
+    ob = oracle.Bound(inst)
+    idx, _ = ob.forward()
+    assert list(idx.reshape(B, S1, 1, topk).shape) == ex["output_shape"]
+    want = _simulated_compressed_counts(S1, S2o, r)
+    assert want[-1] == S2 and want[0] == (S2o - S1 + 1) // r
+    for b in range(B):
+        for i in range(S1):
+            assert ob.visible_count(b, i) == want[i], (b, i)
+            n = valid_prefix_len(idx[b * S1 + i])
+            assert n == min(topk, want[i])
+            assert (idx[b * S1 + i, :n] < want[i]).all()
+
+
+def pin_compressed_counts_closed_form():
+    """Full compressed prefill (S1 = original length, residual 0..r-1): row i
+    sees floor((i + 1) / r) keys; a residual shifts the rows by it."""
+    g = torch.Generator().manual_seed(3)
+    for r, res in ((2, 0), (3, 2), (5, 1)):
+        S2 = 7
+        S1 = S2 * r + res
+        q = torch.randn(1, S1, 2, 128, generator=g).bfloat16()
+        k = torch.randn(1, S2, 1, 128, generator=g).bfloat16()
+        w = torch.randn(1, S1, 2, generator=g).bfloat16()
+        inst = bsnd_inst(q, k, w, topk=4, mask_mode=3)
+        inst["cmp_ratio"] = r
+        inst["cmp_residual_k"] = torch.tensor([res], dtype=torch.int32)
+        ob = oracle.Bound(inst)
+        for i in range(S1):
+            assert ob.visible_count(0, i) == min(S2, (i + 1) // r), (r, res, i)
+        assert _simulated_compressed_counts(S1, S1, r) == [min(S2, (i + 1) // r)
+                                                          for i in range(S1)]
+        inst["mask_mode"] = 0
+        inst["cmp_residual_k"] = None
+        ob0 = oracle.Bound(inst)
+        assert all(ob0.visible_count(0, i) == S2 for i in range(S1))
+
+
+def pin_compression_keeps_scores():
+    """Compression changes which keys are visible, never their scores: a row that
+    sees every key ranks exactly as with mask 0."""
+    g = torch.Generator().manual_seed(4)
+    B, S1, S2, r = 1, 10, 24, 4
+    q = torch.randn(B, S1, 3, 128, generator=g).bfloat16()
+    k = torch.randn(B, S2, 1, 128, generator=g).bfloat16()
+    w = torch.randn(B, S1, 3, generator=g).bfloat16()
+    inst = bsnd_inst(q, k, w, topk=6, mask_mode=3)
+    inst["cmp_ratio"] = r
+    inst["cmp_residual_k"] = torch.tensor([3], dtype=torch.int32)
+    ic, vc = oracle.Bound(inst).forward()
+    i0, v0 = oracle.Bound(bsnd_inst(q, k, w, topk=6, mask_mode=0)).forward()
+    last = S1 - 1            # original position S2*r + 3 - 1 >= every block end
+    assert np.array_equal(ic[last], i0[last]) and np.array_equal(vc[last], v0[last])
+
+
+def pin_output_idx_offset():
+    """output_idx_offset adds the batch's offset to every kept index and leaves the
+    -1 padding and the values alone."""
+    inst = synth.make(synth.Spec(name="off", batch=3, s1=40, s2=40, n1=4, topk=50,
+                                 idx_offset_max=1000), 6)
+    off = inst["output_idx_offset"].numpy()
+    i1, v1 = oracle.Bound(inst).forward()
+    plain = dict(inst)
+    plain["output_idx_offset"] = None
+    i0, v0 = oracle.Bound(plain).forward()
+    assert np.array_equal(v1, v0)
+    for r in range(i0.shape[0]):
+        b = r // 40
+        n = valid_prefix_len(i0[r])
+        assert np.array_equal(i1[r, :n], i0[r, :n] + off[b]) and (i1[r, n:] == -1).all()
 
 
 def pin_thread_count_invariance():

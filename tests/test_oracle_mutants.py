@@ -49,6 +49,10 @@ MUTANTS = {
                        "if (x->score > y->score) return 1;\n  if (x->score < y->score) return -1;"),
     "block_table_batch": ("int blk = in->block_table[(int64_t)b * p->max_blocks_per_seq + s / p->block_size];",
                           "int blk = in->block_table[s / p->block_size];"),
+    "cmp_block_start": ("if ((long long)j * r + r - 1 <= pos) ++n;", "if ((long long)j * r <= pos) ++n;"),
+    "cmp_residual_dropped": ("(long long)S2 * r + in->cmp_residual_k[b] - S1;",
+                             "(long long)S2 * r - S1;"),
+    "idx_offset_dropped": ("oi[j] = c[j].key + off;", "oi[j] = c[j].key;"),
     "w_not_per_token": ("wrow[h] = lio_decode(p->w_dtype, in->w, t * p->n1 + h);",
                         "wrow[h] = lio_decode(p->w_dtype, in->w, h);"),
 }
