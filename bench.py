@@ -183,14 +183,14 @@ def main():
 
     def metadata():
         st = binding.li_metadata(p, ptr(g["cu_seqlens_q"]), ptr(g["cu_seqlens_k"]),
-                                 ptr(g["seqused_k"]), meta.data_ptr(), meta.numel(), sh)
+                                 ptr(g["seqused_k"]), None, meta.data_ptr(), meta.numel(), sh)
         assert st == 0, binding.li_status_str(st)
 
     def forward():
         st = binding.li_forward(p, ptr(g["q"]), ptr(g["k"]), ptr(g["w"]), ptr(g["q_descale"]),
                                 ptr(g["k_descale"]), ptr(g["cu_seqlens_q"]),
-                                ptr(g["cu_seqlens_k"]), ptr(g["seqused_k"]),
-                                ptr(g["block_table"]), meta.data_ptr(), ws.data_ptr(),
+                                ptr(g["cu_seqlens_k"]), ptr(g["seqused_k"]), None,
+                                ptr(g["block_table"]), None, meta.data_ptr(), ws.data_ptr(),
                                 ws.numel(), idx.data_ptr(), val.data_ptr(), sh)
         assert st == 0, binding.li_status_str(st)
 

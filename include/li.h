@@ -60,8 +60,8 @@ extern "C" {
 typedef enum {
   LI_OK = 0,
   LI_ERR_INVALID_ARGUMENT = 1,   /* a value outside the documented range, a missing pointer */
-  LI_ERR_UNSUPPORTED = 2,        /* valid for the pages but not built here (cmp_ratio > 1), or a
-                                    shape whose working set does not fit the kernels */
+  LI_ERR_UNSUPPORTED = 2,        /* valid for the pages but a shape whose working set does not
+                                    fit the kernels (index or token counts past int32) */
   LI_ERR_WORKSPACE_TOO_SMALL = 3,/* metadata or workspace buffer smaller than the size query said */
   LI_ERR_HIP = 4                 /* a HIP runtime call failed (launch error) */
 } li_status;
@@ -105,7 +105,8 @@ typedef struct {
   int32_t block_size;            /* PA only: [1, 1024], block_size*D*elem % 32 == 0         */
   int32_t num_blocks;            /* PA only: blocks in the pool (> 0)                       */
   int32_t max_blocks_per_seq;    /* PA only: columns of block_table (> 0)                   */
-  int32_t cmp_ratio;             /* key compression ratio; only 1 is built                  */
+  int32_t cmp_ratio;             /* >= 1: original key positions per key of k (compressed
+                                    keys); 1 = no compression                              */
   int64_t k_block_stride;        /* PA only: elements between pool blocks, >= block_size*D;
                                     0 means block_size*D (a contiguous pool)                */
 } li_problem;
@@ -125,13 +126,21 @@ li_status li_workspace_size(const li_problem* p, size_t* bytes);
  *                 layout_k == TND, must be NULL otherwise.
  *  seqused_k    : int32 [B], keys used per batch; required iff layout_k == PA_BSND,
  *                 must be NULL otherwise.
+ *  cmp_residual_k : int32 [B], each in [0, cmp_ratio): original keys of the batch
+ *                 past its last compressed key; required iff cmp_ratio > 1 and
+ *                 mask_mode == 3, must be NULL otherwise (aclnnLightningIndexerV2
+ *                 page, 约束说明).  Batch b then has S2_b * cmp_ratio + residual
+ *                 original keys; local row i is original position
+ *                 i + S2_b * cmp_ratio + residual - S1_b and sees key j when
+ *                 j * cmp_ratio + cmp_ratio - 1 is at or before it.
  *  metadata     : device buffer of at least li_metadata_size bytes, 256-byte aligned.
  * The metadata stays valid for any li_forward call with the same problem and the
  * same length arrays; it is read-only for li_forward.
  */
 li_status li_metadata(const li_problem* p, const int32_t* cu_seqlens_q,
-                      const int32_t* cu_seqlens_k, const int32_t* seqused_k, void* metadata,
-                      size_t metadata_bytes, hipStream_t stream);
+                      const int32_t* cu_seqlens_k, const int32_t* seqused_k,
+                      const int32_t* cmp_residual_k, void* metadata, size_t metadata_bytes,
+                      hipStream_t stream);
 
 /*
  * Scores every visible (query, key) pair and writes the per-token top-k.
@@ -143,10 +152,14 @@ li_status li_metadata(const li_problem* p, const int32_t* cu_seqlens_q,
  *  q_descale    : fp32, one per query token ([B, S1] or [T1]); required iff fp8.
  *  k_descale    : fp32, one per key slot ([B, S2], [T2], or [num_blocks, block_size]
  *                 contiguous for the paged pool); required iff fp8.
- *  cu_seqlens_q, cu_seqlens_k, seqused_k : as for li_metadata (same contents).
+ *  cu_seqlens_q, cu_seqlens_k, seqused_k, cmp_residual_k : as for li_metadata
+ *                 (same contents).
  *  block_table  : int32 [B, max_blocks_per_seq]; required iff layout_k == PA_BSND.
  *                 Logical key s of batch b lives in row s % block_size of pool
  *                 block block_table[b][s / block_size].
+ *  output_idx_offset : NULL, or int32 [B] of offsets >= 0 added to every valid
+ *                 index of batch b (the -1 padding stays); index + offset must fit
+ *                 int32 (aclnnLightningIndexerV2 page, 约束说明).
  *  metadata     : filled by li_metadata for this problem.
  *  workspace    : li_workspace_size bytes of device scratch (may be NULL when that
  *                 size is 0), 256-byte aligned; its contents need no initialisation.
@@ -158,7 +171,8 @@ li_status li_metadata(const li_problem* p, const int32_t* cu_seqlens_q,
 li_status li_forward(const li_problem* p, const void* q, const void* k, const void* w,
                      const float* q_descale, const float* k_descale,
                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                     const int32_t* seqused_k, const int32_t* block_table,
+                     const int32_t* seqused_k, const int32_t* cmp_residual_k,
+                     const int32_t* block_table, const int32_t* output_idx_offset,
                      const void* metadata, void* workspace, size_t workspace_bytes,
                      int32_t* sparse_indices, float* sparse_values, hipStream_t stream);
 

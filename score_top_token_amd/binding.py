@@ -66,8 +66,9 @@ def load():
         vp, sz = ctypes.c_void_p, ctypes.c_size_t
         L.li_metadata_size.argtypes = [P, ctypes.POINTER(sz)]
         L.li_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
-        L.li_metadata.argtypes = [P, vp, vp, vp, vp, sz, vp]
-        L.li_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.li_metadata.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+        L.li_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                 vp, vp]
         L.li_status_str.argtypes = [ctypes.c_int]
         L.li_status_str.restype = ctypes.c_char_p
         for n in ("li_metadata_size", "li_workspace_size", "li_metadata", "li_forward"):
@@ -92,18 +93,19 @@ def li_workspace_size(p: Problem) -> tuple[int, int]:
     return st, n.value
 
 
-def li_metadata(p: Problem, cu_seqlens_q, cu_seqlens_k, seqused_k, metadata, metadata_bytes,
-                stream) -> int:
-    return load().li_metadata(ctypes.byref(p), cu_seqlens_q, cu_seqlens_k, seqused_k, metadata,
-                              metadata_bytes, stream)
+def li_metadata(p: Problem, cu_seqlens_q, cu_seqlens_k, seqused_k, cmp_residual_k, metadata,
+                metadata_bytes, stream) -> int:
+    return load().li_metadata(ctypes.byref(p), cu_seqlens_q, cu_seqlens_k, seqused_k,
+                              cmp_residual_k, metadata, metadata_bytes, stream)
 
 
 def li_forward(p: Problem, q, k, w, q_descale, k_descale, cu_seqlens_q, cu_seqlens_k, seqused_k,
-               block_table, metadata, workspace, workspace_bytes, sparse_indices, sparse_values,
-               stream) -> int:
+               cmp_residual_k, block_table, output_idx_offset, metadata, workspace,
+               workspace_bytes, sparse_indices, sparse_values, stream) -> int:
     return load().li_forward(ctypes.byref(p), q, k, w, q_descale, k_descale, cu_seqlens_q,
-                             cu_seqlens_k, seqused_k, block_table, metadata, workspace,
-                             workspace_bytes, sparse_indices, sparse_values, stream)
+                             cu_seqlens_k, seqused_k, cmp_residual_k, block_table,
+                             output_idx_offset, metadata, workspace, workspace_bytes,
+                             sparse_indices, sparse_values, stream)
 
 
 def li_status_str(status: int) -> str:
@@ -165,7 +167,7 @@ def problem_from(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, topk: int, *
 
 
 def lightning_indexer_metadata(p: Problem, *, cu_seqlens_q=None, cu_seqlens_k=None,
-                               seqused_k=None, device=None) -> torch.Tensor:
+                               seqused_k=None, cmp_residual_k=None, device=None) -> torch.Tensor:
     """Allocates and fills the metadata (work list) on the current stream."""
     st, nbytes = li_metadata_size(p)
     _check(st, "li_metadata_size")
@@ -173,13 +175,15 @@ def lightning_indexer_metadata(p: Problem, *, cu_seqlens_q=None, cu_seqlens_k=No
     meta = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     _check(li_metadata(p, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(seqused_k),
-                       meta.data_ptr(), meta.numel(), stream), "li_metadata")
+                       _ptr(cmp_residual_k), meta.data_ptr(), meta.numel(), stream),
+           "li_metadata")
     return meta
 
 
 def lightning_indexer(p: Problem, q, k, w, *, metadata: torch.Tensor, q_descale=None,
                       k_descale=None, cu_seqlens_q=None, cu_seqlens_k=None, seqused_k=None,
-                      block_table=None, return_value: int = 1, workspace=None, out=None):
+                      cmp_residual_k=None, block_table=None, output_idx_offset=None,
+                      return_value: int = 1, workspace=None, out=None):
     """Runs li_forward; returns (sparse_indices, sparse_values or None)."""
     st, ws_bytes = li_workspace_size(p)
     _check(st, "li_workspace_size")
@@ -198,7 +202,8 @@ def lightning_indexer(p: Problem, q, k, w, *, metadata: torch.Tensor, q_descale=
     stream = torch.cuda.current_stream(dev).cuda_stream
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(li_forward(p, _ptr(q), _ptr(k), _ptr(w), _ptr(q_descale), _ptr(k_descale),
-                      _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(seqused_k), _ptr(block_table),
+                      _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(seqused_k),
+                      _ptr(cmp_residual_k), _ptr(block_table), _ptr(output_idx_offset),
                       metadata.data_ptr(), _ptr(workspace), wsb, idx.data_ptr(), _ptr(val),
                       stream), "li_forward")
     return idx, val
@@ -210,7 +215,7 @@ def run_instance(inst: dict, device="cuda", return_value: int = 1):
     dev = torch.device(device)
     g = {n: (inst[n].to(dev) if isinstance(inst.get(n), torch.Tensor) else None)
          for n in ("q", "k", "w", "q_descale", "k_descale", "cu_seqlens_q", "cu_seqlens_k",
-                   "seqused_k", "block_table")}
+                   "seqused_k", "block_table", "cmp_residual_k", "output_idx_offset")}
     if inst["layout_k"] == "PA_BSND":
         # keep the pool's block stride: copy the whole padded pool, then view it
         kc = inst["k"]
@@ -220,11 +225,12 @@ def run_instance(inst: dict, device="cuda", return_value: int = 1):
     p = problem_for(inst, g["k"])
     meta = lightning_indexer_metadata(p, cu_seqlens_q=g["cu_seqlens_q"],
                                       cu_seqlens_k=g["cu_seqlens_k"], seqused_k=g["seqused_k"],
-                                      device=dev)
+                                      cmp_residual_k=g["cmp_residual_k"], device=dev)
     return lightning_indexer(p, g["q"], g["k"], g["w"], metadata=meta, q_descale=g["q_descale"],
                              k_descale=g["k_descale"], cu_seqlens_q=g["cu_seqlens_q"],
                              cu_seqlens_k=g["cu_seqlens_k"], seqused_k=g["seqused_k"],
-                             block_table=g["block_table"], return_value=return_value)
+                             cmp_residual_k=g["cmp_residual_k"], block_table=g["block_table"],
+                             output_idx_offset=g["output_idx_offset"], return_value=return_value)
 
 
 def problem_for(inst: dict, k_dev: Optional[torch.Tensor] = None) -> Problem:
@@ -233,4 +239,5 @@ def problem_for(inst: dict, k_dev: Optional[torch.Tensor] = None) -> Problem:
     return problem_from(inst["q"], k, inst["w"], inst["topk"], layout_q=inst["layout_q"],
                         layout_k=inst["layout_k"], mask_mode=inst["mask_mode"],
                         batch_size=inst["batch"], max_seqlen_q=inst["max_seqlen_q"],
-                        max_seqlen_k=inst["max_seqlen_k"], block_table=inst.get("block_table"))
+                        max_seqlen_k=inst["max_seqlen_k"], block_table=inst.get("block_table"),
+                        cmp_ratio=inst.get("cmp_ratio", 1) or 1)

@@ -15,6 +15,22 @@ __device__ inline int visible_limit(int mask_mode, int i, int s1, int s2) {
   return last >= s2 ? s2 : (int)(last + 1);
 }
 
+// Visible keys of local row i of batch b: the right-down causal prefix, or for
+// compressed keys (cmp_ratio r > 1, lightning_indexer page, parameters and
+// Example) the keys whose r original positions j*r .. j*r + r - 1 all lie at or
+// before the row's original position i + S2*r + residual - S1.
+__device__ inline int row_limit(const KArgs& a, int b, int i, int s1, int s2) {
+  if (a.cmp_ratio <= 1 || a.mask_mode == 0) return visible_limit(a.mask_mode, i, s1, s2);
+  const long long r = a.cmp_ratio;
+  const long long upto = (long long)i + 1 + (long long)s2 * r + a.cmp_res[b] - s1;  // positions <= it
+  if (upto < r) return 0;
+  const long long n = upto / r;
+  return n >= s2 ? s2 : (int)n;
+}
+
+// Offset added to the written indices of batch b (output_idx_offset), else 0.
+__device__ inline int index_offset(const KArgs& a, int b) { return a.idx_off ? a.idx_off[b] : 0; }
+
 // Batch record written by the metadata kernel: {q token offset, S1_b, k token offset, S2_b}.
 __device__ inline int4 batch_rec(const KArgs& a, int b) {
   return reinterpret_cast<const int4*>(a.meta + a.off_batch)[b];

@@ -486,7 +486,7 @@ __device__ __forceinline__ void block_kth(SelShared& sh, const Row& row, int k, 
 // k-th element and stable, index-ordered write of the top-k of one row.
 template <class Row>
 __device__ __forceinline__ void select_row(SelShared& sh, const Row& row, int topk, float lo,
-                                           float hi, int32_t* oi, float* ov) {
+                                           float hi, int32_t* oi, float* ov, int ioff) {
   block_kth(sh, row, topk, lo, hi);
   const float fb = __int_as_float(sh.misc[4]);
   const uint32_t eb = (uint32_t)sh.misc[5];
@@ -506,7 +506,7 @@ __device__ __forceinline__ void select_row(SelShared& sh, const Row& row, int to
     const uint64_t m = ballot(keep);
     const int o = pos + mbcnt(m);
     const bool st = keep & (o < topk);     // bounded whatever the data
-    if (st) oi[o] = p;
+    if (st) oi[o] = p + ioff;
     if (st & has_ov) ov[o] = f;
     pos += __popcll(m);
   });
@@ -521,8 +521,9 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(KArgs a) {
   const int4 br = batch_rec(a, b);
   if (i >= br.y) return;
   const int tid = threadIdx.x;
-  const int lim = visible_limit(a.mask_mode, i, br.y, br.w);
+  const int lim = row_limit(a, b, i, br.y, br.w);
   const int topk = a.topk;
+  const int ioff = index_offset(a, b);
   const int64_t tok = (int64_t)br.x + i;
   int32_t* oi = a.out_idx + tok * topk;
   float* ov = a.out_val ? a.out_val + tok * topk : nullptr;
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(KArgs a) {
   if (lim <= topk) {
     for (int e = tid; e < topk; e += kSelectThreads) {
       if (e < lim) {
-        oi[e] = e;
+        oi[e] = e + ioff;
         if (ov) ov[e] = src[e];
       } else {
         oi[e] = -1;
@@ -555,10 +556,10 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(KArgs a) {
   if (lim <= kRegRowMax) {
     RegRow row;
     row.load(src, lim);
-    select_row(sh, row, topk, lo, hi, oi, ov);
+    select_row(sh, row, topk, lo, hi, oi, ov, ioff);
   } else {
     const GlobalRow row{src, lim};
-    select_row(sh, row, topk, lo, hi, oi, ov);
+    select_row(sh, row, topk, lo, hi, oi, ov, ioff);
   }
 }
 

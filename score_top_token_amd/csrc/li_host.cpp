@@ -38,7 +38,6 @@ li_status validate_scalars(const li_problem* p) {
     return LI_ERR_INVALID_ARGUMENT;
   if (p->w_dtype != LI_DT_BF16 && p->w_dtype != LI_DT_FP32) return LI_ERR_INVALID_ARGUMENT;
   if (p->cmp_ratio < 1) return LI_ERR_INVALID_ARGUMENT;
-  if (p->cmp_ratio != 1) return LI_ERR_UNSUPPORTED;
   if (p->layout_q == LI_LAYOUT_TND && p->total_q < 0) return LI_ERR_INVALID_ARGUMENT;
   if (p->layout_k == LI_LAYOUT_TND && p->total_k < 0) return LI_ERR_INVALID_ARGUMENT;
   if (p->layout_k == LI_LAYOUT_PA_BSND) {
@@ -151,7 +150,10 @@ bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 // (aclnnLightningIndexerV2 page, 约束说明: cu_seqlens only with TND layouts,
 // seqused_k required with, and only with, the paged key layout).
 li_status validate_lengths(const li_problem* p, const int32_t* cu_q, const int32_t* cu_k,
-                           const int32_t* seqused_k) {
+                           const int32_t* seqused_k, const int32_t* cmp_res) {
+  // the compression residuals come with, and only with, compressed keys under mask 3
+  if ((p->cmp_ratio > 1 && p->mask_mode == 3) != (cmp_res != nullptr))
+    return LI_ERR_INVALID_ARGUMENT;
   if ((p->layout_q == LI_LAYOUT_TND) != (cu_q != nullptr)) return LI_ERR_INVALID_ARGUMENT;
   if ((p->layout_k == LI_LAYOUT_TND) != (cu_k != nullptr)) return LI_ERR_INVALID_ARGUMENT;
   if ((p->layout_k == LI_LAYOUT_PA_BSND) != (seqused_k != nullptr)) return LI_ERR_INVALID_ARGUMENT;
@@ -174,6 +176,7 @@ KArgs base_args(const li_problem* p, const Plan& pl, void* metadata) {
   a.max_blocks_per_seq = p->max_blocks_per_seq;
   const int64_t kbs = p->k_block_stride ? p->k_block_stride : (int64_t)p->block_size * kHeadDim;
   a.k_block_stride_bytes = kbs * elem_bytes(p->qk_dtype);
+  a.cmp_ratio = p->cmp_ratio;
   a.block_shift = -1;
   if (p->block_size > 0 && (p->block_size & (p->block_size - 1)) == 0)
     a.block_shift = __builtin_ctz((unsigned)p->block_size);
@@ -214,12 +217,12 @@ li_status li_workspace_size(const li_problem* p, size_t* bytes) {
 }
 
 li_status li_metadata(const li_problem* p, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                      const int32_t* seqused_k, void* metadata, size_t metadata_bytes,
-                      hipStream_t stream) {
+                      const int32_t* seqused_k, const int32_t* cmp_residual_k, void* metadata,
+                      size_t metadata_bytes, hipStream_t stream) {
   Plan pl;
   li_status st = make_plan(p, &pl);
   if (st != LI_OK) return st;
-  st = validate_lengths(p, cu_seqlens_q, cu_seqlens_k, seqused_k);
+  st = validate_lengths(p, cu_seqlens_q, cu_seqlens_k, seqused_k, cmp_residual_k);
   if (st != LI_OK) return st;
   if (!metadata || !aligned(metadata, 16)) return LI_ERR_INVALID_ARGUMENT;
   if (metadata_bytes < pl.meta_bytes) return LI_ERR_WORKSPACE_TOO_SMALL;
@@ -228,19 +231,21 @@ li_status li_metadata(const li_problem* p, const int32_t* cu_seqlens_q, const in
   a.cu_q = cu_seqlens_q;
   a.cu_k = cu_seqlens_k;
   a.seqused_k = seqused_k;
+  a.cmp_res = cmp_residual_k;
   return launch_metadata(a, pl.mode, stream) == hipSuccess ? LI_OK : LI_ERR_HIP;
 }
 
 li_status li_forward(const li_problem* p, const void* q, const void* k, const void* w,
                      const float* q_descale, const float* k_descale, const int32_t* cu_seqlens_q,
                      const int32_t* cu_seqlens_k, const int32_t* seqused_k,
-                     const int32_t* block_table, const void* metadata, void* workspace,
+                     const int32_t* cmp_residual_k, const int32_t* block_table,
+                     const int32_t* output_idx_offset, const void* metadata, void* workspace,
                      size_t workspace_bytes, int32_t* sparse_indices, float* sparse_values,
                      hipStream_t stream) {
   Plan pl;
   li_status st = make_plan(p, &pl);
   if (st != LI_OK) return st;
-  st = validate_lengths(p, cu_seqlens_q, cu_seqlens_k, seqused_k);
+  st = validate_lengths(p, cu_seqlens_q, cu_seqlens_k, seqused_k, cmp_residual_k);
   if (st != LI_OK) return st;
   if ((p->layout_k == LI_LAYOUT_PA_BSND) != (block_table != nullptr)) return LI_ERR_INVALID_ARGUMENT;
   const bool fp8 = p->qk_dtype == LI_DT_FP8_E4M3;
@@ -263,6 +268,8 @@ li_status li_forward(const li_problem* p, const void* q, const void* k, const vo
   a.cu_q = cu_seqlens_q;
   a.cu_k = cu_seqlens_k;
   a.seqused_k = seqused_k;
+  a.cmp_res = cmp_residual_k;
+  a.idx_off = output_idx_offset;
   a.ws = static_cast<float*>(workspace);
   if (pl.mode == kModeDecode)
     a.seg_mm = a.ws + (size_t)p->batch * p->max_seqlen_q * pl.ws_row_stride;

@@ -76,6 +76,8 @@ struct KArgs {
   const int32_t* cu_q;
   const int32_t* cu_k;
   const int32_t* seqused_k;
+  const int32_t* cmp_res;   // compressed keys under mask 3: residual original keys per batch
+  const int32_t* idx_off;   // NULL or an index offset per batch
   unsigned char* meta;      // metadata base
   float* ws;                // decode: dense score rows
   float* seg_mm;            // decode: (min, max) score of each segment, seg_mm_stride pairs per row
@@ -85,7 +87,7 @@ struct KArgs {
   int64_t ws_row_stride;
   int32_t seg_mm_stride;
   int32_t batch, s1max, s2max;
-  int32_t n1, topk;
+  int32_t n1, topk, cmp_ratio;
   int32_t layout_q, layout_k, mask_mode;
   int32_t block_size, block_shift, max_blocks_per_seq;
   int32_t cap, dcap, chunk, max_items, rows_per_item;

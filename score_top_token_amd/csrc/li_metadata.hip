@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
     bt[b] = int4{q_off, s1, k_off, s2};
     if (small) s_bt[b] = int4{q_off, s1, k_off, s2};
     if (mode == kModeDecode)
-      for (int i = 0; i < s1; ++i) vis += visible_limit(a.mask_mode, i, s1, s2);
+      for (int i = 0; i < s1; ++i) vis += row_limit(a, b, i, s1, s2);
   }
   // decode segment length: the shortest multiple of 32 keys for which the
   // segments of all rows number at most `target` (one per wave of a full GPU,
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
       for (int b = tid / kChunkCands; b < B; b += kMetaThreads / kChunkCands) {
         const int4 rec = get_bt(b);
         for (int i = 0; i < rec.y; ++i)
-          nseg += ((uint32_t)visible_limit(a.mask_mode, i, rec.y, rec.w) + c - 1u) / c;
+          nseg += ((uint32_t)row_limit(a, b, i, rec.y, rec.w) + c - 1u) / c;
       }
       for (int o = kChunkCands; o < 64; o <<= 1) nseg += __shfl_xor(nseg, o);
       if (lane < kChunkCands && nseg) atomicAdd(&s_cand[lane], nseg);
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
     const int4 rec = get_bt(b);
     int cnt = 0;
     if (mode == kModeDecode) {
-      for (int i = 0; i < rec.y; ++i) cnt += cdiv(visible_limit(a.mask_mode, i, rec.y, rec.w), chunk);
+      for (int i = 0; i < rec.y; ++i) cnt += cdiv(row_limit(a, b, i, rec.y, rec.w), chunk);
     } else {
       cnt = cdiv(rec.y, a.rows_per_item);
     }
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
         if (b < B) {
           const int4 rec = get_bt(b);
           for (int i = 0; i < rec.y; ++i)
-            pc[q] += (visible_limit(a.mask_mode, i, rec.y, rec.w) % chunk) != 0;
+            pc[q] += (row_limit(a, b, i, rec.y, rec.w) % chunk) != 0;
         }
         sum += pc[q];
       }
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
     } else {
       int rest = r, i = 0, lim = 0, part = 0;
       for (; i < rec.y; ++i) {
-        lim = visible_limit(a.mask_mode, i, rec.y, rec.w);
+        lim = row_limit(a, b, i, rec.y, rec.w);
         const int nch = cdiv(lim, chunk);
         if (rest < nch) break;
         rest -= nch;

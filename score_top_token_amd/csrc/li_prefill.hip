@@ -36,9 +36,10 @@ __device__ inline float canon(float f) {
 
 // Writes the top-k of a score row in ascending key order, given its k-th element.
 // vals: LDS scores; idx: LDS keys or nullptr (key = position).  At most topk
-// entries are written whatever the data.
+// entries are written whatever the data; each index plus ioff (the batch's
+// output index offset).
 __device__ inline void write_kept(const float* vals, const uint32_t* idx, int n, float fb,
-                                  uint32_t eb, int32_t* oi, float* ov, int topk) {
+                                  uint32_t eb, int32_t* oi, float* ov, int topk, int ioff) {
   const int l = lane_id();
   int kept = 0;
   for (int p0 = 0; p0 < n; p0 += 64) {
@@ -55,7 +56,7 @@ __device__ inline void write_kept(const float* vals, const uint32_t* idx, int n,
     if (keep) {
       const int pos = kept + mbcnt(m);
       if (pos < topk) {
-        oi[pos] = (int32_t)e;
+        oi[pos] = (int32_t)e + ioff;
         if (ov) ov[pos] = f;
       }
     }
@@ -74,7 +75,7 @@ __device__ inline void write_padding(int n, int topk, int32_t* oi, float* ov) {
 // from the list once the k-th element is known, then the padding.
 __device__ inline void write_list_topk(const float* listF, const uint32_t* listI, int count,
                                        int topk, uint32_t* hist, uint32_t* scr, int32_t* oi,
-                                       float* ov) {
+                                       float* ov, int ioff) {
   const int lane = lane_id();
   if (count > topk) {
     float vmin = __builtin_inff(), vmax = -__builtin_inff();
@@ -86,11 +87,11 @@ __device__ inline void write_list_topk(const float* listF, const uint32_t* listI
     float fb;
     uint32_t eb;
     wave_kth(listF, listI, count, topk, wave_min_f(vmin), wave_max_f(vmax), hist, scr, fb, eb);
-    write_kept(listF, listI, count, fb, eb, oi, ov, topk);
+    write_kept(listF, listI, count, fb, eb, oi, ov, topk, ioff);
     return;
   }
   for (int e = lane; e < count; e += 64) {
-    oi[e] = (int32_t)listI[e];
+    oi[e] = (int32_t)listI[e] + ioff;
     if (ov) ov[e] = listF[e];
   }
   write_padding(count, topk, oi, ov);
@@ -120,13 +121,14 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
   const int4 br = batch_rec(a, b);               // q_off, s1, k_off, s2
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int topk = a.topk;
+  const int ioff = index_offset(a, b);
 
   float* row = reinterpret_cast<float*>(smem + R0) + wave * a.dcap;
 
   const bool has_row = wave < nrows;
   const int i = q0 + wave;
-  const int lim = has_row ? visible_limit(a.mask_mode, i, br.y, br.w) : 0;
-  const int kend = visible_limit(a.mask_mode, q0 + nrows - 1, br.y, br.w);
+  const int lim = has_row ? row_limit(a, b, i, br.y, br.w) : 0;
+  const int kend = row_limit(a, b, q0 + nrows - 1, br.y, br.w);
   const int ntiles = (kend + kPipeKeys - 1) / kPipeKeys;
   const int64_t tok = (int64_t)br.x + i;
   const bool direct = lim <= topk;
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
     const int s = t * kPipeKeys + lane;
     if (lane < 32 && s < lim) {
       if (direct) {
-        oi[s] = s;
+        oi[s] = s + ioff;
         if (ov) ov[s] = tot + 0.0f;        // -0 -> +0
       } else {
         const float f = canon(tot);
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
   float fb;
   uint32_t eb;
   wave_kth(row, nullptr, lim, topk, wave_min_f(vmin), wave_max_f(vmax), hist, scr, fb, eb);
-  write_kept(row, nullptr, lim, fb, eb, oi, ov, topk);
+  write_kept(row, nullptr, lim, fb, eb, oi, ov, topk, ioff);
 }
 
 // ---------------------------------------------------------------------------
@@ -257,6 +259,7 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_shared_kernel(KAr
   const int4 br = batch_rec(a, b);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int cap = a.cap, topk = a.topk;
+  const int ioff = index_offset(a, b);
 
   // LDS: two K tiles, the descale slots, the per-wave select scratch, the lists
   constexpr int SCR = 2 * TILE + (QK == DT_FP8 ? kDscSlots * 32 * 4 : 0);
@@ -268,8 +271,8 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_shared_kernel(KAr
 
   const bool has_row = wave < nrows;
   const int i = q0 + wave;
-  const int lim = has_row ? visible_limit(a.mask_mode, i, br.y, br.w) : 0;
-  const int kend = visible_limit(a.mask_mode, q0 + nrows - 1, br.y, br.w);
+  const int lim = has_row ? row_limit(a, b, i, br.y, br.w) : 0;
+  const int kend = row_limit(a, b, q0 + nrows - 1, br.y, br.w);
   const int ntiles = (kend + kPipeKeys - 1) / kPipeKeys;
   const int64_t tok = (int64_t)br.x + i;
 
@@ -417,7 +420,7 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_shared_kernel(KAr
   if (!has_row) return;
   int32_t* oi = a.out_idx + tok * topk;
   float* ov = a.out_val ? a.out_val + tok * topk : nullptr;
-  write_list_topk(listF, listI, count, topk, hist, scr, oi, ov);
+  write_list_topk(listF, listI, count, topk, hist, scr, oi, ov, ioff);
 }
 
 // stream_kernel (fp8 keys; every key dtype when a large topk leaves room for
@@ -445,8 +448,9 @@ __global__ __launch_bounds__(W * 64, 1) void stream_kernel(KArgs a) {
   if (wave >= nrows) return;
   const int4 br = batch_rec(a, b);
   const int cap = a.cap, topk = a.topk;
+  const int ioff = index_offset(a, b);
   const int i = q0 + wave;
-  const int lim = visible_limit(a.mask_mode, i, br.y, br.w);
+  const int lim = row_limit(a, b, i, br.y, br.w);
   const int64_t tok = (int64_t)br.x + i;
   int32_t* oi = a.out_idx + tok * topk;
   float* ov = a.out_val ? a.out_val + tok * topk : nullptr;
@@ -590,7 +594,7 @@ __global__ __launch_bounds__(W * 64, 1) void stream_kernel(KArgs a) {
     emit(last, QK == DT_FP8 ? sc * dcur : sc);
   }
 
-  write_list_topk(listF, listI, count, topk, hist, scr, oi, ov);
+  write_list_topk(listF, listI, count, topk, hist, scr, oi, ov, ioff);
 }
 
 template <class K>

@@ -58,6 +58,7 @@ class Spec:
     len_lo: int = 0
     len_hi: int = 0
     kv_extra: int = 0
+    kv_div: int = 1                # TND keys = queries // kv_div + kv_extra (compressed keys)
     # PA_BSND: one query row per sequence by default (decode); key lengths drawn
     # uniformly in [len_lo, len_hi]; pool holds batch*max_blocks_per_seq blocks.
     block_size: int = 128
@@ -152,7 +153,7 @@ def make(spec: Spec | str, seed: int = 0) -> dict:
             lq = [int(v) for v in spec.fixed_lengths]
         else:
             lq = torch.randint(spec.len_lo, spec.len_hi + 1, (B,), generator=g).tolist()
-        lk = [v + spec.kv_extra for v in lq]
+        lk = [v // spec.kv_div + spec.kv_extra for v in lq]
         out["seqlens_q"], out["seqlens_k"] = lq, lk
         out["total_q"], out["total_k"] = sum(lq), sum(lk)
         out["max_seqlen_q"], out["max_seqlen_k"] = max(lq) if lq else 0, max(lk) if lk else 0

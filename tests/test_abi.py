@@ -61,7 +61,7 @@ def pa_problem(**kw):
     (dict(layout_q=2), INVALID), (dict(layout_k=7), INVALID),
     (dict(qk_dtype=2), INVALID), (dict(qk_dtype=1), OK), (dict(qk_dtype=3), OK),
     (dict(w_dtype=1), INVALID), (dict(w_dtype=2), OK),
-    (dict(cmp_ratio=4), UNSUPPORTED), (dict(cmp_ratio=0), INVALID),
+    (dict(cmp_ratio=4), OK), (dict(cmp_ratio=0), INVALID),
     (dict(batch=-1), INVALID), (dict(max_seqlen_q=-1), INVALID),
     (dict(batch=0), OK),
 ])
@@ -103,34 +103,34 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails va
 def test_metadata_pointer_rules():
     p = base_problem()
     _, mb = binding.li_metadata_size(p)
-    assert binding.li_metadata(p, None, None, None, None, mb, None) == INVALID
-    assert binding.li_metadata(p, FAKE, None, None, FAKE, mb, None) == INVALID   # cu_q with BSND
-    assert binding.li_metadata(p, None, FAKE, None, FAKE, mb, None) == INVALID   # cu_k with BSND
-    assert binding.li_metadata(p, None, None, FAKE, FAKE, mb, None) == INVALID   # seqused_k w/o PA
-    assert binding.li_metadata(p, None, None, None, FAKE, mb - 1, None) == TOO_SMALL
-    assert binding.li_metadata(p, None, None, None, FAKE + 1, mb, None) == INVALID  # misaligned
+    assert binding.li_metadata(p, None, None, None, None, None, mb, None) == INVALID
+    assert binding.li_metadata(p, FAKE, None, None, None, FAKE, mb, None) == INVALID   # cu_q with BSND
+    assert binding.li_metadata(p, None, FAKE, None, None, FAKE, mb, None) == INVALID   # cu_k with BSND
+    assert binding.li_metadata(p, None, None, FAKE, None, FAKE, mb, None) == INVALID   # seqused_k w/o PA
+    assert binding.li_metadata(p, None, None, None, None, FAKE, mb - 1, None) == TOO_SMALL
+    assert binding.li_metadata(p, None, None, None, None, FAKE + 1, mb, None) == INVALID  # misaligned
     tnd = base_problem(layout_q=1, layout_k=1, total_q=10, total_k=10)
     _, mt = binding.li_metadata_size(tnd)
-    assert binding.li_metadata(tnd, None, FAKE, None, FAKE, mt, None) == INVALID  # TND needs cu_q
-    assert binding.li_metadata(tnd, FAKE, None, None, FAKE, mt, None) == INVALID  # TND needs cu_k
+    assert binding.li_metadata(tnd, None, FAKE, None, None, FAKE, mt, None) == INVALID  # TND needs cu_q
+    assert binding.li_metadata(tnd, FAKE, None, None, None, FAKE, mt, None) == INVALID  # TND needs cu_k
     pa = pa_problem()
     _, mp = binding.li_metadata_size(pa)
-    assert binding.li_metadata(pa, None, None, None, FAKE, mp, None) == INVALID   # PA needs seqused_k
+    assert binding.li_metadata(pa, None, None, None, None, FAKE, mp, None) == INVALID   # PA needs seqused_k
 
 
 def test_forward_pointer_rules():
     p = base_problem()
     _, mb = binding.li_metadata_size(p)
     F = FAKE
-    args = dict(q=F, k=F, w=F, qd=None, kd=None, cq=None, ck=None, su=None, bt=None, meta=F,
-                ws=None, wsb=0, idx=F, val=F)
+    args = dict(q=F, k=F, w=F, qd=None, kd=None, cq=None, ck=None, su=None, cr=None, bt=None,
+                off=None, meta=F, ws=None, wsb=0, idx=F, val=F)
 
     def call(prob=p, **over):
         a = dict(args)
         a.update(over)
         return binding.li_forward(prob, a["q"], a["k"], a["w"], a["qd"], a["kd"], a["cq"], a["ck"],
-                                  a["su"], a["bt"], a["meta"], a["ws"], a["wsb"], a["idx"],
-                                  a["val"], None)
+                                  a["su"], a["cr"], a["bt"], a["off"], a["meta"], a["ws"],
+                                  a["wsb"], a["idx"], a["val"], None)
 
     assert call(q=None) == INVALID
     assert call(k=None) == INVALID
@@ -149,19 +149,22 @@ def test_forward_pointer_rules():
     assert call(prob=pa, su=F) == INVALID                 # PA needs block_table
     assert call(prob=pa, su=F, bt=F, ws=F, wsb=wb - 1) == TOO_SMALL
     assert call(prob=pa, su=F, bt=F, ws=None, wsb=wb) == INVALID
-    assert call(prob=base_problem(cmp_ratio=4)) == UNSUPPORTED
+    cmp = base_problem(cmp_ratio=4)                       # compressed keys, mask 3
+    assert call(prob=cmp) == INVALID                      # needs cmp_residual_k
+    assert call(cr=F) == INVALID                          # residuals only with compression
+    assert call(prob=base_problem(cmp_ratio=4, mask_mode=0), cr=F) == INVALID   # not with mask 0
 
 
 def test_empty_problem_launches_nothing():
     # zero query rows: LI_OK without touching the (fake) buffers or the device
     p = base_problem(batch=0)
     _, mb = binding.li_metadata_size(p)
-    assert binding.li_metadata(p, None, None, None, FAKE, mb, None) == OK
-    assert binding.li_forward(p, FAKE, FAKE, FAKE, None, None, None, None, None, None, FAKE,
-                              None, 0, FAKE, None, None) == OK
+    assert binding.li_metadata(p, None, None, None, None, FAKE, mb, None) == OK
+    assert binding.li_forward(p, FAKE, FAKE, FAKE, None, None, None, None, None, None, None,
+                              None, FAKE, None, 0, FAKE, None, None) == OK
     tnd = base_problem(layout_q=1, layout_k=1, total_q=0, total_k=0, batch=3)
     _, mt = binding.li_metadata_size(tnd)
-    assert binding.li_metadata(tnd, FAKE, FAKE, None, FAKE, mt, None) == OK
+    assert binding.li_metadata(tnd, FAKE, FAKE, None, None, FAKE, mt, None) == OK
 
 
 def test_problem_struct_matches_header():

@@ -53,7 +53,10 @@ def structural_check(gi, gv, inst, ob):
     for b in range(inst["batch"]):
         s1, s2 = inst["seqlens_q"][b], inst["seqlens_k"][b]
         i = np.arange(s1)
-        v = np.full(s1, s2) if inst["mask_mode"] == 0 else np.clip(i + s2 - s1 + 1, 0, s2)
+        if (inst.get("cmp_ratio") or 1) > 1:         # compressed keys: the oracle's rule
+            v = np.array([ob.visible_count(b, x) for x in range(s1)], dtype=np.int64)
+        else:
+            v = np.full(s1, s2) if inst["mask_mode"] == 0 else np.clip(i + s2 - s1 + 1, 0, s2)
         vis[r:r + s1] = v
         r += s1
     assert r == nrows
@@ -70,14 +73,32 @@ def structural_check(gi, gv, inst, ob):
         assert np.isfinite(gv[valid]).all(), "non-finite value"
 
 
+def _without_offsets(idx, inst):
+    """Valid indices minus their batch's output index offset (checked to be
+    there); padding untouched."""
+    off = inst.get("output_idx_offset")
+    if off is None:
+        return idx
+    per_row = np.repeat(off.numpy().astype(np.int64), inst["seqlens_q"])
+    valid = idx >= 0
+    assert (idx[valid] >= np.broadcast_to(per_row[:, None], idx.shape)[valid]).all(), \
+        "index below its batch offset"
+    return np.where(valid, idx - per_row[:, None], idx).astype(np.int32)
+
+
 def compare_all(inst, rows=None, return_value=1, seed_rows=0):
     gi, gv = _gpu(inst, return_value)
     ob = oracle.Bound(inst)
+    gi = _without_offsets(gi, inst)
     structural_check(gi, gv, inst, ob)
     if rows is None:
         rows = np.arange(gi.shape[0])
     rows = np.asarray(rows, dtype=np.int64)
     oi, ov = ob.forward(rows=rows, nthreads=ORACLE_THREADS)
+    if inst.get("output_idx_offset") is not None:
+        per_row = np.repeat(inst["output_idx_offset"].numpy().astype(np.int64),
+                            inst["seqlens_q"])[rows]
+        oi = np.where(oi >= 0, oi - per_row[:, None], oi).astype(np.int32)
     rep = compare.check_rows(gi[rows], None if gv is None else gv[rows], oi, ov, rows, ob)
     _say(f"    rows={rep.rows} max_abs={rep.max_abs:.3g} max_rel={rep.max_rel:.3g} "
          f"swaps={rep.swaps}")
@@ -134,6 +155,28 @@ SMALL = {
                                         qk_dtype="fp8", w_scale=0.125)),
     "k8192_decode": (None, 27, dict(batch=4, s1=1, n1=64, topk=8192, layout_k="PA_BSND",
                                     len_lo=5000, len_hi=20000, block_size=128, w_scale=0.125)),
+    # compressed keys (cmp_ratio): the pages' example (130 original keys -> 32 with
+    # residual 2), a longer dense case, the streaming kernel, TND with per-sequence
+    # residuals, decode rows with compression; output index offsets on every path
+    "cmp_pages_example": (None, 28, dict(batch=2, s1=64, s2=32, n1=16, topk=32,
+                                         qk_dtype="fp16", w_dtype="fp32", cmp_ratio=4,
+                                         fixed_residuals=[2, 2])),
+    "cmp_dense": (None, 29, dict(batch=1, s1=4003, s2=1000, n1=64, topk=256, cmp_ratio=4,
+                                 w_scale=0.125)),
+    "cmp_stream": (None, 30, dict(batch=1, s1=200, s2=12000, n1=64, topk=512, cmp_ratio=3,
+                                  w_scale=0.125)),
+    "cmp_tnd": (None, 31, dict(batch=3, n1=24, topk=64, layout_q="TND", layout_k="TND",
+                               len_lo=200, len_hi=1500, kv_div=4, cmp_ratio=4)),
+    "cmp_decode": (None, 32, dict(batch=5, s1=3, n1=64, topk=128, layout_k="PA_BSND",
+                                  len_lo=300, len_hi=3000, block_size=64, cmp_ratio=2,
+                                  w_scale=0.125)),
+    "idx_offset_dense": (None, 33, dict(batch=3, s1=300, s2=300, n1=16, topk=64,
+                                        idx_offset_max=1 << 20)),
+    "idx_offset_stream": (None, 34, dict(batch=1, s1=40, s2=11000, n1=64, topk=512,
+                                         idx_offset_max=1 << 20, w_scale=0.125)),
+    "idx_offset_decode": (None, 35, dict(batch=6, s1=1, n1=64, topk=200, layout_k="PA_BSND",
+                                         len_lo=100, len_hi=4000, block_size=128,
+                                         idx_offset_max=1 << 20, w_scale=0.125)),
 }
 
 
