@@ -103,13 +103,25 @@ li_status make_plan(const li_problem* p, Plan* pl) {
     pl->seg_mm_stride = (int32_t)cdiv64(std::max(p->max_seqlen_k, 1), kTileKeys);
     pl->ws_bytes = (size_t)B * p->max_seqlen_q * ((size_t)pl->ws_row_stride * 4 + (size_t)pl->seg_mm_stride * 8);
     pl->lds_select = select_shared_bytes();
-  } else if (dense_lds <= kLdsBudget) {
+  } else if (dense_lds <= kLdsBudget / 2) {
+    // two workgroups per CU
     pl->mode = kModeDense;
     pl->rows_per_item = kDenseWaves;
     pl->dcap = (int32_t)dcap;
     pl->lds_prefill = dense_lds;
     items = prefill_items(p, kDenseWaves);
+  } else if ((size_t)kDenseSlots * kDenseWaves * dcap * 4 <= kDenseGlobalMaxBytes) {
+    // rows too long for LDS: the same kernel with each row in a global workspace
+    // row, one per wave of a fixed grid of resident workgroups
+    pl->mode = kModeDenseGlobal;
+    pl->rows_per_item = kDenseWaves;
+    items = prefill_items(p, kDenseWaves);
+    pl->grid = (int32_t)std::min<int64_t>(items, kDenseSlots);
+    pl->ws_row_stride = dcap;
+    pl->ws_bytes = (size_t)pl->grid * kDenseWaves * dcap * 4;
+    pl->lds_prefill = std::max(tiles, (size_t)kDenseWaves * kWideScratch);
   } else {
+    // rows past the workspace cap (over 262144 keys): bounded candidate lists
     pl->mode = kModeStream;
     // Four rows per workgroup.  fp8: a 32-key K tile and the select scratch per
     // wave, then the lists; otherwise two shared 32-key K tiles, the select
@@ -281,7 +293,8 @@ li_status li_forward(const li_problem* p, const void* q, const void* k, const vo
                  : (p->block_size % 32 == 0 ? KL_PAGED_TILE : KL_PAGED);
   hipError_t e;
   if (pl.mode != kModeDecode) {
-    e = launch_prefill(a, pl.mode, qk, wt, pl.mblocks, kl, pl.max_items, pl.lds_prefill, stream);
+    const int grid = pl.mode == kModeDenseGlobal ? pl.grid : pl.max_items;
+    e = launch_prefill(a, pl.mode, qk, wt, pl.mblocks, kl, grid, pl.lds_prefill, stream);
   } else {
     e = launch_decode(a, qk, wt, pl.mblocks, kl,
                       (int)cdiv64(pl.max_items, kDecodeWaves), stream);

@@ -25,9 +25,14 @@ constexpr int kSelectThreads = 1024;    // decode-mode select kernel
 constexpr int kSelectBuckets = 2048;    // decode-mode select: histogram buckets
 constexpr size_t kLdsBudget = 160 * 1024;
 constexpr int kWaveScratch = 256 * 4 + 2 * 64 * 4;   // per-wave select scratch: histogram + gather
+// dense kernel with rows in global memory: per-wave 2048-bucket histogram, gather
+// scratch and the 256-bucket histogram of the fallback select
+constexpr int kWideScratch = 2048 * 4 + 2 * 64 * 4 + 256 * 4;
+constexpr int kDenseSlots = 512;         // resident dense workgroups: 2 per CU on 256 CUs
+constexpr size_t kDenseGlobalMaxBytes = size_t(1) << 31;   // workspace cap of that mode
 constexpr int kMetaMagic = 0x4C494D44;  // "LIMD"
 
-enum Mode : int32_t { kModeDense = 0, kModeStream = 1, kModeDecode = 2 };
+enum Mode : int32_t { kModeDense = 0, kModeStream = 1, kModeDecode = 2, kModeDenseGlobal = 3 };
 
 // Metadata buffer layout (all int32 / int4 records, offsets in bytes):
 //   [0, 256)        header, see MetaHeader
@@ -63,6 +68,7 @@ struct Plan {
   size_t ws_bytes;
   int64_t ws_row_stride;  // decode: fp32 slots per (batch, row) score row
   int32_t seg_mm_stride;  // decode: segment (min, max) pairs per row
+  int32_t grid;           // dense rows in global memory: resident workgroups
 };
 
 // Kernel argument block (passed by value).

@@ -9,7 +9,11 @@
 //     causal masking) are dispatched first, round-robin over the batches with
 //     the batch order rotated every round (workgroups are dealt to the 8 XCDs by
 //     index mod 8: without the rotation a batch count that is a multiple of 8
-//     would send every block of one batch to one XCD);
+//     would send every block of one batch to one XCD).  The dense kernel with
+//     rows in global memory walks the list with a stride of its fixed grid, so
+//     there the list is batch-major instead (longest sequence first, each from
+//     its last block): at any time every XCD works on one sequence, whose keys
+//     then stay in its L2;
 //   - decode mode: the visible keys of every query row cut into segments of one
 //     length, the shortest for which all rows together need at most
 //     kDecodeSegments segments; one item per segment.  The split kernel runs
@@ -53,6 +57,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
   __shared__ int s_part[kMetaThreads / 64];
   __shared__ int s_pstart[kRoundRobinMaxBatch];   // decode: partial segments before batch b
   __shared__ int s_npart;                          // decode: all partial segments
+  __shared__ int s_gstart[kRoundRobinMaxBatch];    // batch-major prefill: first item of batch b
   __shared__ unsigned long long s_cand[kChunkCands], s_tot, s_nrows;
   __shared__ int s_total, s_chunk;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -229,6 +234,18 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
     }
     n_slots = min((total + kXcdRound - 1) / kXcdRound * kXcdRound, a.max_items);
   }
+  if (small && mode == kModeDenseGlobal) {
+    // batches by query rows, descending (ties by index): items before batch b
+    for (int b = tid; b < B; b += kMetaThreads) {
+      const int len = s_bt[b].y;
+      int before = 0;
+      for (int bb = 0; bb < B; ++bb) {
+        const int l2 = s_bt[bb].y;
+        before += (l2 > len || (l2 == len && bb < b)) ? s_counts[bb] : 0;
+      }
+      s_gstart[b] = before;
+    }
+  }
   if (tid == 0) {
     hdr->n_items = n_slots;
     hdr->mode = mode;
@@ -256,7 +273,9 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
       const int q0 = blk * a.rows_per_item;
       const int nrows = min(a.rows_per_item, rec.y - q0);
       int pos = u;
-      if (small) {
+      if (small && mode == kModeDenseGlobal) {
+        pos = s_gstart[b] + r;
+      } else if (small) {
         // round-robin over batches, each batch walked from its last block.
         // Round r holds the n_r batches with more than r blocks; their order
         // is rotated by r, so that a batch does not land on the same XCD

@@ -64,6 +64,24 @@ __device__ inline void write_kept(const float* vals, const uint32_t* idx, int n,
   }
 }
 
+// write_kept for a row in global memory, the index of entry p being p.
+__device__ inline void write_kept_row(const float* vals, int n, float fb, uint32_t eb,
+                                      int32_t* oi, float* ov, int topk, int ioff) {
+  int kept = 0;
+  row_pass(vals, n, [&](int p, bool valid, float f) __attribute__((always_inline)) {
+    const bool keep = valid && (f > fb || (f == fb && (uint32_t)p <= eb));
+    const uint64_t m = ballot(keep);
+    if (keep) {
+      const int pos = kept + mbcnt(m);
+      if (pos < topk) {
+        oi[pos] = p + ioff;
+        if (ov) ov[pos] = f;
+      }
+    }
+    kept += __popcll(m);
+  });
+}
+
 __device__ inline void write_padding(int n, int topk, int32_t* oi, float* ov) {
   for (int e = n + lane_id(); e < topk; e += 64) {
     oi[e] = -1;
@@ -98,32 +116,37 @@ __device__ inline void write_list_topk(const float* listF, const uint32_t* listI
 }
 
 // ---------------------------------------------------------------------------
-// dense kernel: 4 rows per workgroup, scores of a row kept densely in LDS
+// dense kernel: 4 rows per workgroup, every score of a row kept densely, in
+// LDS (G = false) or, for rows too long for LDS, in a global workspace row per
+// wave of each resident workgroup (G = true; the grid is then one workgroup per
+// slot, two per CU, each walking the work list with a stride of the grid).
 // ---------------------------------------------------------------------------
-template <int QK, int MB, int WT, int KL>
-__global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
+template <int QK, int MB, int WT, int KL, bool G>
+__device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char* smem) {
   typedef Mma<QK> M;
   typedef typename M::frag F;
   constexpr int NT = kDenseWaves * 64;
   constexpr int TILE = kPipeKeys * M::RB;
   // [0, R0): two K tiles and the descale slots during the score loop, the
-  // per-wave select scratch afterwards; then the score rows
+  // per-wave select scratch afterwards; then (G = false) the score rows
   constexpr int DSC = 2 * TILE;                      // descale slots (fp8 only)
   constexpr int R0a = DSC + (QK == DT_FP8 ? kDscSlots * 32 * 4 : 0);
-  constexpr int R0 = R0a > kDenseWaves * kWaveScratch ? R0a : kDenseWaves * kWaveScratch;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr int SCR = G ? kWideScratch : kWaveScratch;
+  constexpr int R0 = R0a > kDenseWaves * SCR ? R0a : kDenseWaves * SCR;
   float* dsc_lds = reinterpret_cast<float*>(smem + DSC);
 
-  const MetaHeader* hdr = reinterpret_cast<const MetaHeader*>(a.meta);
-  if ((int)blockIdx.x >= hdr->n_items) return;
-  const int4 item = reinterpret_cast<const int4*>(a.meta + a.off_items)[blockIdx.x];
+  // opaque per item: lane-derived offsets are recomputed in each item instead of
+  // being hoisted out of the item loop and held through the score loop
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int topk = a.topk;
+  float* row = G ? a.ws + ((int64_t)blockIdx.x * kDenseWaves + wave) * a.ws_row_stride
+                 : reinterpret_cast<float*>(smem + R0) + wave * a.dcap;
+  const int4 item = reinterpret_cast<const int4*>(a.meta + a.off_items)[it];
   const int b = item.x, q0 = item.y, nrows = item.z;
   const int4 br = batch_rec(a, b);               // q_off, s1, k_off, s2
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int topk = a.topk;
   const int ioff = index_offset(a, b);
-
-  float* row = reinterpret_cast<float*>(smem + R0) + wave * a.dcap;
 
   const bool has_row = wave < nrows;
   const int i = q0 + wave;
@@ -228,12 +251,37 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
     write_padding(lim, topk, oi, ov);
     return;
   }
-  uint32_t* hist = reinterpret_cast<uint32_t*>(smem + wave * kWaveScratch);
-  uint32_t* scr = hist + 256;
   float fb;
   uint32_t eb;
-  wave_kth(row, nullptr, lim, topk, wave_min_f(vmin), wave_max_f(vmax), hist, scr, fb, eb);
-  write_kept(row, nullptr, lim, fb, eb, oi, ov, topk, ioff);
+  const float lo = wave_min_f(vmin), hi = wave_max_f(vmax);
+  if constexpr (G) {
+    uint32_t* hist = reinterpret_cast<uint32_t*>(smem + wave * kWideScratch);
+    uint32_t* scr = hist + kWideBuckets;
+    if (!wave_topk_row(row, lim, topk, lo, hi, hist, scr, oi, ov, ioff)) {
+      wave_kth(row, nullptr, lim, topk, lo, hi, scr + 2 * kSelSmall, scr, fb, eb);
+      write_kept_row(row, lim, fb, eb, oi, ov, topk, ioff);
+    }
+  } else {
+    uint32_t* hist = reinterpret_cast<uint32_t*>(smem + wave * kWaveScratch);
+    uint32_t* scr = hist + 256;
+    wave_kth(row, nullptr, lim, topk, lo, hi, hist, scr, fb, eb);
+    write_kept(row, nullptr, lim, fb, eb, oi, ov, topk, ioff);
+  }
+}
+
+template <int QK, int MB, int WT, int KL, bool G>
+__global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int n_items = reinterpret_cast<const MetaHeader*>(a.meta)->n_items;
+  if constexpr (!G) {
+    if ((int)blockIdx.x < n_items) dense_item<QK, MB, WT, KL, G>(a, blockIdx.x, smem);
+  } else {
+    for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+      // the previous item's select scratch overlaps the K tiles
+      if (it != (int)blockIdx.x) __syncthreads();
+      dense_item<QK, MB, WT, KL, G>(a, it, smem);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -609,7 +657,9 @@ hipError_t launch_kernel(K fn, int nthreads, int grid, size_t lds, hipStream_t s
 template <int QK, int MB, int WT, int KL>
 hipError_t launch_one(const KArgs& a, int mode, int grid, size_t lds, hipStream_t s) {
   if (mode == kModeDense)
-    return launch_kernel(dense_kernel<QK, MB, WT, KL>, kDenseWaves * 64, grid, lds, s, a);
+    return launch_kernel(dense_kernel<QK, MB, WT, KL, false>, kDenseWaves * 64, grid, lds, s, a);
+  if (mode == kModeDenseGlobal)
+    return launch_kernel(dense_kernel<QK, MB, WT, KL, true>, kDenseWaves * 64, grid, lds, s, a);
   if (a.rows_per_item == kStreamWavesLarge)
     return launch_kernel(stream_kernel<QK, MB, WT, KL, kStreamWavesLarge>, kStreamWavesLarge * 64,
                          grid, lds, s, a);

@@ -239,4 +239,148 @@ __device__ inline void wave_kth(const float* vals, const uint32_t* idx, int n, i
   }
 }
 
+// ---------------------------------------------------------------------------
+// Selection over a score row in global memory (one wave per row).  Each pass
+// keeps kRowUnroll loads in flight per lane, since every load is an L2 round
+// trip; one histogram of kWideBuckets linear buckets usually leaves at most
+// kSelSmall values in the bucket of the k-th element.
+// ---------------------------------------------------------------------------
+constexpr int kRowUnroll = 16;
+constexpr int kWideBuckets = 2048;
+
+// Linear value bucket in [0, kWideBuckets); halving first keeps (hi - lo) finite.
+struct FBucketWide {
+  float lo2, scale;
+  __device__ FBucketWide(float lo, float hi) {
+    lo2 = lo * 0.5f;
+    scale = fminf((float)kWideBuckets / (hi * 0.5f - lo2), 3.0e38f);
+  }
+  __device__ uint32_t operator()(float f) const {
+    const float x = fminf((f * 0.5f - lo2) * scale, (float)(kWideBuckets - 1));
+    return (uint32_t)fmaxf(x, 0.0f);
+  }
+};
+
+// f(p, valid, v) over vals[0, n) (n >= 1) in index order, kRowUnroll * 64
+// entries per round, lane l holding entry p = round start + 64 u + l.  Calls
+// are wave-uniform (f may ballot); lanes past n get valid = false.
+template <class F>
+__device__ __forceinline__ void row_pass(const float* vals, int n, F f) {
+  const int l = lane_id();
+  for (int p0 = 0; p0 < n; p0 += 64 * kRowUnroll) {
+    float v[kRowUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int p = p0 + 64 * u + l;
+      v[u] = vals[p < n ? p : n - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int p = p0 + 64 * u + l;
+      if (p0 + 64 * u < n) f(p, p < n, v[u]);
+    }
+  }
+}
+
+// wave_find_bucket over kWideBuckets counts (lane l owns buckets 32l .. 32l+31).
+__device__ inline void wave_find_bucket_wide(const uint32_t* hist, int r, int& bkt, int& above,
+                                             int& cnt) {
+  const int l = lane_id();
+  const uint32_t* h = hist + 32 * l;
+  int s = 0;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) s += (int)h[j];
+  const int suf = wave_suffix_sum(s);
+  const int ab = suf - s;
+  const bool mine = ab < r && r <= suf;
+  int b = 0, a = 0, c = 0;
+  if (mine) {
+    int acc = ab;
+    for (int j = 31; j >= 0; --j) {
+      const int hj = (int)h[j];
+      if (acc + hj >= r) {
+        b = 32 * l + j;
+        a = acc;
+        c = hj;
+        break;
+      }
+      acc += hj;
+    }
+  }
+  const uint64_t who = ballot(mine);
+  const int src = who ? (int)__builtin_ctzll(who) : 0;
+  bkt = __shfl(b, src);
+  above = __shfl(a, src);
+  cnt = __shfl(c, src);
+}
+
+// Top-k of a global score row vals[0, n) whose values lie in [lo, hi] (the
+// index of entry p is p; k < n), written to oi / ov (indices plus ioff) in two
+// passes: a histogram of kWideBuckets buckets finds the bucket B of the k-th
+// element; the second pass writes every entry of a bucket above B (all kept, in
+// index order) and gathers bucket B, whose exact rank then decides which of its
+// entries follow them.  Returns false, writing nothing, when lo == hi or bucket B
+// holds more than kSelSmall entries.  hist: kWideBuckets u32 and scr:
+// 2 * kSelSmall words of LDS private to the wave.
+__device__ inline bool wave_topk_row(const float* vals, int n, int k, float lo, float hi,
+                                     uint32_t* hist, uint32_t* scr, int32_t* oi, float* ov,
+                                     int ioff) {
+  if (!(lo < hi)) return false;
+  const int l = lane_id();
+  const FBucketWide fbk(lo, hi);
+  for (int x = l; x < kWideBuckets; x += 64) hist[x] = 0;
+  wave_sync();
+  row_pass(vals, n, [&](int, bool valid, float f) __attribute__((always_inline)) {
+    if (valid) atomicAdd(&hist[fbk(f)], 1u);
+  });
+  wave_sync();
+  int B, above, cnt;
+  wave_find_bucket_wide(hist, k, B, above, cnt);
+  wave_sync();
+  if (cnt > kSelSmall) return false;
+  float* sf = reinterpret_cast<float*>(scr);
+  uint32_t* se = scr + kSelSmall;
+  int pos = 0, got = 0;
+  row_pass(vals, n, [&](int p, bool valid, float f) __attribute__((always_inline)) {
+    const uint32_t bk = fbk(f);
+    const bool up = valid && bk > (uint32_t)B;
+    const uint64_t mu = ballot(up);
+    if (up) {
+      const int o = pos + mbcnt(mu);
+      if (o < k) {
+        oi[o] = p + ioff;
+        if (ov) ov[o] = f;
+      }
+    }
+    pos += __popcll(mu);
+    const bool take = valid && bk == (uint32_t)B;
+    const uint64_t mt = ballot(take);
+    if (take) {
+      const int slot = got + mbcnt(mt);
+      if (slot < kSelSmall) {
+        sf[slot] = f;
+        se[slot] = (uint32_t)p;
+      }
+    }
+    got += __popcll(mt);
+  });
+  wave_sync();
+  const int m = got < kSelSmall ? got : kSelSmall;
+  const float cf = l < m ? sf[l] : 0.0f;
+  const uint32_t ce = l < m ? se[l] : 0u;
+  wave_sync();
+  float fb;
+  uint32_t eb;
+  wave_rank_small(cf, ce, m, k - above, fb, eb);
+  // the gathered entries are in index order: the kept ones follow the others
+  const bool keep = l < m && (cf > fb || (cf == fb && ce <= eb));
+  const uint64_t mk = ballot(keep);
+  const int o = above + mbcnt(mk);
+  if (keep && o < k) {
+    oi[o] = (int32_t)ce + ioff;
+    if (ov) ov[o] = cf;
+  }
+  return true;
+}
+
 }  // namespace li

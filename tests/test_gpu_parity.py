@@ -174,6 +174,14 @@ SMALL = {
                                         idx_offset_max=1 << 20)),
     "idx_offset_stream": (None, 34, dict(batch=1, s1=40, s2=11000, n1=64, topk=512,
                                          idx_offset_max=1 << 20, w_scale=0.125)),
+    # rows past 262144 keys: the streaming kernels (bf16 / fp16 shared tiles, fp8
+    # per wave, and two rows per workgroup at topk 8192)
+    "stream_long_bf16": (None, 36, dict(batch=1, s1=6, s2=270000, n1=8, topk=300,
+                                        idx_offset_max=1000)),
+    "stream_long_fp8": (None, 37, dict(batch=1, s1=5, s2=263000, n1=16, topk=512,
+                                       qk_dtype="fp8", w_scale=0.25)),
+    "stream_long_k8192": (None, 38, dict(batch=1, s1=5, s2=265000, n1=8, topk=8192,
+                                         qk_dtype="fp16", w_dtype="fp32")),
     "idx_offset_decode": (None, 35, dict(batch=6, s1=1, n1=64, topk=200, layout_k="PA_BSND",
                                          len_lo=100, len_hi=4000, block_size=128,
                                          idx_offset_max=1 << 20, w_scale=0.125)),
@@ -364,7 +372,7 @@ def test_prefill_work_list(spec):
     blocks of a single batch only."""
     inst = synth.make(synth.Spec(name="wlp", **spec), 3)
     hdr, items = _meta_items(inst)
-    assert hdr[1] in (0, 1)                               # dense or streaming
+    assert hdr[1] in (0, 1, 3)                            # dense, streaming, dense with global rows
     rows = 4
     want = set()
     for b in range(spec["batch"]):
