@@ -200,9 +200,9 @@ struct PipeStage {
 };
 
 // K ring depth (tiles in flight; 2 or 4).  The dense kernel runs two
-// workgroups per CU, whose register budget leaves room for 2; the streaming
-// kernel runs one workgroup per CU and reads K from the infinity cache, so it
-// keeps 4 tiles in flight.
+// workgroups per CU, whose register budget leaves room for 2 bf16 / fp16 tiles
+// (it keeps 4 of the half-size fp8 tiles); the streaming kernels run one
+// workgroup per CU and keep 4 tiles in flight.
 constexpr int kStageDepth = 2;
 constexpr int kDscSlots = 4;      // tile t's descales live in slot t % 4 from step t-1 to t+1
 constexpr int kStreamStageDepth = 4;

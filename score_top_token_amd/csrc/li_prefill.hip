@@ -158,7 +158,8 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
   int32_t* oi = a.out_idx + tok * topk;
   float* ov = a.out_val ? a.out_val + tok * topk : nullptr;
 
-  constexpr int D = kStageDepth;
+  // fp8 tiles are half the registers: four in flight hide more of the L2 / MALL latency
+  constexpr int D = QK == DT_FP8 ? 4 : kStageDepth;
   PipeStage<QK, KL, NT, D> st;
   st.prefetch_table(a, b, 0);
   F qf[MB][M::KSTEPS];
