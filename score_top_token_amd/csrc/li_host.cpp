@@ -89,7 +89,7 @@ li_status make_plan(const li_problem* p, Plan* pl) {
   // two 32-key K tiles and, for fp8, the descale slots (4 x 32 floats), or the
   // per-wave select scratch, whichever is larger; then the score rows
   const size_t tiles = 2 * (size_t)kPipeKeys * rb + (p->qk_dtype == LI_DT_FP8_E4M3 ? 4 * 32 * 4 : 0);
-  const size_t dense_r0 = std::max(tiles, (size_t)kDenseWaves * kWaveScratch);
+  const size_t dense_r0 = std::max(tiles, (size_t)kDenseWaves * kDenseScratch);
   const size_t dense_lds = dense_r0 + (size_t)kDenseWaves * dcap * 4;
   int64_t items;
   if (use_decode(p)) {

@@ -25,6 +25,7 @@ constexpr int kSelectThreads = 1024;    // decode-mode select kernel
 constexpr int kSelectBuckets = 2048;    // decode-mode select: histogram buckets
 constexpr size_t kLdsBudget = 160 * 1024;
 constexpr int kWaveScratch = 256 * 4 + 2 * 64 * 4;   // per-wave select scratch: histogram + gather
+constexpr int kDenseScratch = 512 * 4 + 2 * 64 * 4;  // dense kernel, rows in LDS: 512-bucket histogram + gather
 // dense kernel with rows in global memory: per-wave 2048-bucket histogram, gather
 // scratch and the 256-bucket histogram of the fallback select
 constexpr int kWideScratch = 2048 * 4 + 2 * 64 * 4 + 256 * 4;

@@ -131,7 +131,7 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
   // per-wave select scratch afterwards; then (G = false) the score rows
   constexpr int DSC = 2 * TILE;                      // descale slots (fp8 only)
   constexpr int R0a = DSC + (QK == DT_FP8 ? kDscSlots * 32 * 4 : 0);
-  constexpr int SCR = G ? kWideScratch : kWaveScratch;
+  constexpr int SCR = G ? kWideScratch : kDenseScratch;
   constexpr int R0 = R0a > kDenseWaves * SCR ? R0a : kDenseWaves * SCR;
   float* dsc_lds = reinterpret_cast<float*>(smem + DSC);
 
@@ -258,15 +258,17 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
   if constexpr (G) {
     uint32_t* hist = reinterpret_cast<uint32_t*>(smem + wave * kWideScratch);
     uint32_t* scr = hist + kWideBuckets;
-    if (!wave_topk_row(row, lim, topk, lo, hi, hist, scr, oi, ov, ioff)) {
+    if (!wave_topk_row<kWideBuckets>(row, lim, topk, lo, hi, hist, scr, oi, ov, ioff)) {
       wave_kth(row, nullptr, lim, topk, lo, hi, scr + 2 * kSelSmall, scr, fb, eb);
       write_kept_row(row, lim, fb, eb, oi, ov, topk, ioff);
     }
   } else {
-    uint32_t* hist = reinterpret_cast<uint32_t*>(smem + wave * kWaveScratch);
-    uint32_t* scr = hist + 256;
-    wave_kth(row, nullptr, lim, topk, lo, hi, hist, scr, fb, eb);
-    write_kept(row, nullptr, lim, fb, eb, oi, ov, topk, ioff);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(smem + wave * kDenseScratch);
+    uint32_t* scr = hist + kLdsBuckets;
+    if (!wave_topk_row<kLdsBuckets>(row, lim, topk, lo, hi, hist, scr, oi, ov, ioff)) {
+      wave_kth(row, nullptr, lim, topk, lo, hi, hist, scr, fb, eb);
+      write_kept(row, nullptr, lim, fb, eb, oi, ov, topk, ioff);
+    }
   }
 }
 

@@ -240,23 +240,27 @@ __device__ inline void wave_kth(const float* vals, const uint32_t* idx, int n, i
 }
 
 // ---------------------------------------------------------------------------
-// Selection over a score row in global memory (one wave per row).  Each pass
-// keeps kRowUnroll loads in flight per lane, since every load is an L2 round
-// trip; one histogram of kWideBuckets linear buckets usually leaves at most
-// kSelSmall values in the bucket of the k-th element.
+// Two-pass top-k of a dense score row (one wave per row), in global memory or
+// in LDS.  Each pass keeps kRowUnroll loads in flight per lane (for a global
+// row every load is an L2 round trip); one histogram of NB linear buckets
+// usually leaves at most kSelSmall values in the bucket of the k-th element:
+// kWideBuckets for rows of up to 262144 keys in global memory, kLdsBuckets for
+// rows of up to 4096 keys in LDS.
 // ---------------------------------------------------------------------------
 constexpr int kRowUnroll = 16;
 constexpr int kWideBuckets = 2048;
+constexpr int kLdsBuckets = 512;
 
-// Linear value bucket in [0, kWideBuckets); halving first keeps (hi - lo) finite.
-struct FBucketWide {
+// Linear value bucket in [0, NB); halving first keeps (hi - lo) finite.
+template <int NB>
+struct FBucketN {
   float lo2, scale;
-  __device__ FBucketWide(float lo, float hi) {
+  __device__ FBucketN(float lo, float hi) {
     lo2 = lo * 0.5f;
-    scale = fminf((float)kWideBuckets / (hi * 0.5f - lo2), 3.0e38f);
+    scale = fminf((float)NB / (hi * 0.5f - lo2), 3.0e38f);
   }
   __device__ uint32_t operator()(float f) const {
-    const float x = fminf((f * 0.5f - lo2) * scale, (float)(kWideBuckets - 1));
+    const float x = fminf((f * 0.5f - lo2) * scale, (float)(NB - 1));
     return (uint32_t)fmaxf(x, 0.0f);
   }
 };
@@ -282,24 +286,26 @@ __device__ __forceinline__ void row_pass(const float* vals, int n, F f) {
   }
 }
 
-// wave_find_bucket over kWideBuckets counts (lane l owns buckets 32l .. 32l+31).
-__device__ inline void wave_find_bucket_wide(const uint32_t* hist, int r, int& bkt, int& above,
-                                             int& cnt) {
+// wave_find_bucket over NB counts (lane l owns buckets NB/64 * l .. NB/64 * (l+1) - 1).
+template <int NB>
+__device__ inline void wave_find_bucket_n(const uint32_t* hist, int r, int& bkt, int& above,
+                                          int& cnt) {
+  constexpr int PER = NB / 64;
   const int l = lane_id();
-  const uint32_t* h = hist + 32 * l;
+  const uint32_t* h = hist + PER * l;
   int s = 0;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) s += (int)h[j];
+  for (int j = 0; j < PER; ++j) s += (int)h[j];
   const int suf = wave_suffix_sum(s);
   const int ab = suf - s;
   const bool mine = ab < r && r <= suf;
   int b = 0, a = 0, c = 0;
   if (mine) {
     int acc = ab;
-    for (int j = 31; j >= 0; --j) {
+    for (int j = PER - 1; j >= 0; --j) {
       const int hj = (int)h[j];
       if (acc + hj >= r) {
-        b = 32 * l + j;
+        b = PER * l + j;
         a = acc;
         c = hj;
         break;
@@ -314,28 +320,29 @@ __device__ inline void wave_find_bucket_wide(const uint32_t* hist, int r, int& b
   cnt = __shfl(c, src);
 }
 
-// Top-k of a global score row vals[0, n) whose values lie in [lo, hi] (the
+// Top-k of a dense score row vals[0, n) whose values lie in [lo, hi] (the
 // index of entry p is p; k < n), written to oi / ov (indices plus ioff) in two
-// passes: a histogram of kWideBuckets buckets finds the bucket B of the k-th
+// passes: a histogram of NB buckets finds the bucket B of the k-th
 // element; the second pass writes every entry of a bucket above B (all kept, in
 // index order) and gathers bucket B, whose exact rank then decides which of its
 // entries follow them.  Returns false, writing nothing, when lo == hi or bucket B
-// holds more than kSelSmall entries.  hist: kWideBuckets u32 and scr:
-// 2 * kSelSmall words of LDS private to the wave.
+// holds more than kSelSmall entries.  hist: NB u32 and scr: 2 * kSelSmall
+// words of LDS private to the wave.
+template <int NB>
 __device__ inline bool wave_topk_row(const float* vals, int n, int k, float lo, float hi,
                                      uint32_t* hist, uint32_t* scr, int32_t* oi, float* ov,
                                      int ioff) {
   if (!(lo < hi)) return false;
   const int l = lane_id();
-  const FBucketWide fbk(lo, hi);
-  for (int x = l; x < kWideBuckets; x += 64) hist[x] = 0;
+  const FBucketN<NB> fbk(lo, hi);
+  for (int x = l; x < NB; x += 64) hist[x] = 0;
   wave_sync();
   row_pass(vals, n, [&](int, bool valid, float f) __attribute__((always_inline)) {
     if (valid) atomicAdd(&hist[fbk(f)], 1u);
   });
   wave_sync();
   int B, above, cnt;
-  wave_find_bucket_wide(hist, k, B, above, cnt);
+  wave_find_bucket_n<NB>(hist, k, B, above, cnt);
   wave_sync();
   if (cnt > kSelSmall) return false;
   float* sf = reinterpret_cast<float*>(scr);
