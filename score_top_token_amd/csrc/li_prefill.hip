@@ -214,10 +214,12 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
     // set S (tile t) went to LDS in the previous step: refill it first, so
     // the wait for tile t+1 below leaves D-1 tiles in flight
     st.template load<S>(a, b, br.z, (t + D) * kPipeKeys, kend, tid);
-    st.template store<(S + 1) % D>(smem + ((t + 1) & 1) * TILE, tid);
-    st.template store_dsc<(S + 1) % D>(dsc_lds + ((t + 1) & (kDscSlots - 1)) * 32, tid);
+    // tile t's fragments are read before tile t+1 is stored, so that the
+    // MFMAs' reads do not queue behind the stores in the LDS
     F kb[M::KSTEPS];
     read_tile_frags<QK>(smem + (t & 1) * TILE, lane, kb);
+    st.template store<(S + 1) % D>(smem + ((t + 1) & 1) * TILE, tid);
+    st.template store_dsc<(S + 1) % D>(dsc_lds + ((t + 1) & (kDscSlots - 1)) * 32, tid);
     const float ds = QK == DT_FP8 ? dsc_lds[((t - 1) & (kDscSlots - 1)) * 32 + (lane & 31)] : 1.0f;
     mma_tile<QK, MB>(qf, kb, cur);
     const float prev_score = block_score<MB>(prev, wv);
