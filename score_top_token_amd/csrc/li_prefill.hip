@@ -168,22 +168,26 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
   else zero_query<QK, MB>(qf, wv);
   settle_loads();
 
-  // results of tile t (descaled): lanes 0-31 carry keys t*32 + lane.  Rows that
-  // need the select also track their minimum and maximum here.
+  // results of tile t (descaled): lanes 0-31 carry keys t*32 + lane, lanes
+  // 32-63 the same scores again.  Every row's scores go to its row (the rows
+  // that need no select are copied out after the loop), so a step's memory
+  // operations never depend on the row: a data-dependent global store inside
+  // the loop would make every wait for the K ring wait for it as well.  The
+  // row's minimum and maximum are tracked here.
   float vmin = __builtin_inff(), vmax = -__builtin_inff();
   auto emit = [&](int t, float tot) {
-    const int s = t * kPipeKeys + lane;
-    if (lane < 32 && s < lim) {
-      if (direct) {
-        oi[s] = s + ioff;
-        if (ov) ov[s] = tot + 0.0f;        // -0 -> +0
-      } else {
-        const float f = canon(tot);
-        row[s] = f;
-        vmin = fminf(vmin, f);
-        vmax = fmaxf(vmax, f);
-      }
+    const int s = t * kPipeKeys + (lane & 31);
+    const bool in = lane < 32 && s < lim;
+    const float f = canon(tot);
+    if constexpr (G) {
+      // every lane stores (lanes 32-63 repeat lanes 0-31); keys past lim land
+      // below the row stride, in slots that are never read
+      row[s] = f;
+    } else {
+      if (in) row[s] = f;
     }
+    vmin = in ? fminf(vmin, f) : vmin;
+    vmax = in ? fmaxf(vmax, f) : vmax;
   };
 
   f32x16 accA[MB], accB[MB];
@@ -251,6 +255,15 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
   __syncthreads();                         // the tile area becomes select scratch
   if (!has_row) return;
   if (direct) {
+    // every visible key is kept: the row in key order, then the padding
+    if (lim > 0) {
+      row_pass(row, lim, [&](int p, bool valid, float f) __attribute__((always_inline)) {
+        if (valid) {
+          oi[p] = p + ioff;
+          if (ov) ov[p] = f;
+        }
+      });
+    }
     write_padding(lim, topk, oi, ov);
     return;
   }
