@@ -204,34 +204,38 @@ def test_return_value_zero_gives_same_indices():
     assert np.array_equal(gi0, gi1)
 
 
-def test_all_zero_scores_pick_smallest_indices():
-    S, topk = 300, 50
-    q = torch.zeros(1, S, 8, 128).bfloat16()
+# (S1, S2): rows in LDS, and rows long enough for the workspace rows of the dense kernel
+@pytest.mark.parametrize("s1,s2", [(300, 300), (40, 6000)])
+def test_all_zero_scores_pick_smallest_indices(s1, s2):
+    topk = 50
+    q = torch.zeros(1, s1, 8, 128).bfloat16()
     g = torch.Generator().manual_seed(0)
-    k = torch.randn(1, S, 1, 128, generator=g).bfloat16()
-    w = torch.rand(1, S, 8, generator=g).bfloat16()
+    k = torch.randn(1, s2, 1, 128, generator=g).bfloat16()
+    w = torch.rand(1, s1, 8, generator=g).bfloat16()
     inst = bsnd_inst(q, k, w, topk=topk, mask_mode=3)
     inst["name"] = "zero_scores"
     gi, gv = _gpu(inst)
-    for i in range(S):
-        n = min(topk, i + 1)
+    for i in range(s1):
+        n = min(topk, i + s2 - s1 + 1)
         assert list(gi[i, :n]) == list(range(n))
         assert (gv[i, :n] == 0).all() and not np.signbit(gv[i, :n]).any()
 
 
-def test_integer_scores_exact_with_ties():
+@pytest.mark.parametrize("s1,s2,topk", [(500, 500, 37), (48, 6000, 300)])
+def test_integer_scores_exact_with_ties(s1, s2, topk):
     # small integers: every score is an exact integer in fp32, so the GPU must
-    # equal the oracle exactly, ties at the k-th place included
+    # equal the oracle exactly, ties at the k-th place included (many equal
+    # scores: the bucket of the k-th element holds more than a gather's worth)
     g = torch.Generator().manual_seed(1)
-    B, S, N1, topk = 2, 500, 16, 37
-    q = int_tensor(g, (B, S, N1, 128), -1, 1)
-    k = int_tensor(g, (B, S, 1, 128), -1, 1)
-    w = int_tensor(g, (B, S, N1), -2, 3)
+    B, N1 = 2, 16
+    q = int_tensor(g, (B, s1, N1, 128), -1, 1)
+    k = int_tensor(g, (B, s2, 1, 128), -1, 1)
+    w = int_tensor(g, (B, s1, N1), -2, 3)
     inst = bsnd_inst(q, k, w, topk=topk, mask_mode=3)
     inst["name"] = "integer_ties"
     gi, gv = _gpu(inst)
     oi, ov = oracle.Bound(inst).forward(nthreads=ORACLE_THREADS)
-    for r in range(B * S):
+    for r in range(B * s1):
         n = int((oi[r] >= 0).sum())
         order = np.argsort(gi[r, :n], kind="stable")
         assert sorted(gi[r, :n].tolist()) == sorted(oi[r, :n].tolist()), f"row {r}"
@@ -241,11 +245,13 @@ def test_integer_scores_exact_with_ties():
 
 
 def test_determinism_bitwise():
-    spec = synth.Spec(name="det", batch=1, s1=600, s2=600, n1=64, topk=128, w_scale=0.125)
-    inst = synth.make(spec, 21)
-    a = _gpu(inst)
-    b = _gpu(inst)
-    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    for s1, s2 in ((600, 600), (64, 9000)):
+        spec = synth.Spec(name="det", batch=1, s1=s1, s2=s2, n1=64, topk=128, w_scale=0.125)
+        inst = synth.make(spec, 21)
+        a = _gpu(inst)
+        b = _gpu(inst)
+        assert np.array_equal(a[0], b[0])
+        assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
     dec = synth.Spec(name="det_dec", batch=3, s1=1, n1=64, topk=256, layout_k="PA_BSND",
                      len_lo=1000, len_hi=4000, block_size=128, w_scale=0.125)
     inst = synth.make(dec, 22)
