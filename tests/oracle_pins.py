@@ -480,6 +480,55 @@ def pin_output_idx_offset():
         assert np.array_equal(i1[r, :n], i0[r, :n] + off[b]) and (i1[r, n:] == -1).all()
 
 
+def pin_gather_closed_form():
+    """Gathering rows that hold their own token number returns the selected token
+    numbers: index i with block size bs gives tokens i*bs .. i*bs + bs - 1, -1
+    and tokens past the sequence give zero rows (aclnnSparseFlashAttentionGrad
+    page, calculation formula)."""
+    from oracle.gather import gather
+    for layout, extra in (("BSND", {}), ("TND", dict(layout_q="TND", layout_k="TND", len_lo=9,
+                                                     len_hi=30)),
+                          ("PA_BSND", dict(layout_k="PA_BSND", len_lo=9, len_hi=30,
+                                           block_size=4, block_pad=1))):
+        inst = synth.make(synth.Spec(name="g", batch=3, s1=5, s2=21, n1=2, topk=6, **extra), 2)
+        B = inst["batch"]
+        # every key slot's row = 16 bytes of 1 + its position + 40 * its sequence
+        if layout == "PA_BSND":
+            nb, bsz = inst["num_blocks"], inst["block_size"]
+            kv = np.zeros((nb, bsz, 16), dtype=np.uint8)
+            bt = inst["block_table"].numpy()
+            for b in range(B):
+                for s in range(inst["seqlens_k"][b]):
+                    kv[bt[b, s // bsz], s % bsz, :] = s + 1 + 40 * b
+        elif layout == "TND":
+            kv = np.zeros((sum(inst["seqlens_k"]), 16), dtype=np.uint8)
+            o = 0
+            for b in range(B):
+                for s in range(inst["seqlens_k"][b]):
+                    kv[o + s, :] = s + 1 + 40 * b
+                o += inst["seqlens_k"][b]
+        else:
+            kv = np.zeros((B, inst["max_seqlen_k"], 16), dtype=np.uint8)
+            for b in range(B):
+                for s in range(inst["max_seqlen_k"]):
+                    kv[b, s, :] = s + 1 + 40 * b
+        rows = sum(inst["seqlens_q"])
+        g = np.random.default_rng(7)
+        for sb in (1, 3):
+            idx = g.integers(-1, 10, size=(rows, 6)).astype(np.int32)
+            out = gather(inst, kv, idx, sb)
+            r = 0
+            for b in range(B):
+                for _ in range(inst["seqlens_q"][b]):
+                    for j in range(6):
+                        for u in range(sb):
+                            s = idx[r, j] * sb + u
+                            want = (0 if idx[r, j] < 0 or s >= inst["seqlens_k"][b]
+                                    else s + 1 + 40 * b)
+                            assert (out[r, j * sb + u] == want).all(), (layout, sb, r, j, u)
+                    r += 1
+
+
 def pin_thread_count_invariance():
     inst = synth.make("tiny", seed=1)
     ob = oracle.Bound(inst)

@@ -83,3 +83,26 @@ def test_mutant_is_caught(name, source, tmp_path):
             except AssertionError:
                 failed.append(pin.__name__)
     assert failed, f"mutant {name} passed every pin"
+
+
+# Planted mistakes in the gather oracle (oracle/gather.py): each must fail its pin.
+GATHER_SRC = os.path.join(os.path.dirname(oracle.__file__), "gather.py")
+GATHER_MUTANTS = {
+    "tnd_offset_dropped": ("src = kv[k0 + s]", "src = kv[s]"),
+    "block_size_ignored": ("s = sel * select_block + u", "s = sel + u"),
+    "pool_row_wrong": ("src = kv[blk, s % bs]", "src = kv[blk, s // bs]"),
+    "padding_index_used": ("if sel < 0:\n                    continue", "if sel < -1:\n                    continue"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GATHER_MUTANTS))
+def test_gather_mutant_is_caught(name, monkeypatch):
+    import oracle.gather as og
+    old, new = GATHER_MUTANTS[name]
+    src = open(GATHER_SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique / missing"
+    ns = {}
+    exec(compile(src.replace(old, new), "gather_mutant", "exec"), ns)
+    monkeypatch.setattr(og, "gather", ns["gather"])
+    with pytest.raises((AssertionError, IndexError)):
+        oracle_pins.pin_gather_closed_form()
