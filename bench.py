@@ -13,6 +13,9 @@ and the CPU oracle timed on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload prefill|decode|varlen|longfp8|tiny]
                   [--no-cpu-baseline] [--gpus 1]
+
+--workload gather times li_gather instead: the rows that the decode workload's
+top-2048 selects, gathered from a paged pool of 1 KiB token rows (HBM-bound).
 """
 from __future__ import annotations
 
@@ -43,7 +46,7 @@ WARMUP_MIN_S = 0.5
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["li_device.h", "li_common_kernels.h", "li_pipe.h", "li_select.h",
                   "li_prefill.hip", "li_decode.hip", "li_metadata.hip", "li_host.cpp",
-                  "li_internal.h"]
+                  "li_internal.h", "li_gather.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -138,7 +141,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="prefill", choices=sorted(synth.PRESETS))
+    ap.add_argument("--workload", default="prefill", choices=sorted(synth.PRESETS) + ["gather"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
@@ -164,6 +167,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     binding.load()
+    if args.workload == "gather":
+        bench_gather(args, dev)
+        return
     inst = synth.make(args.workload, args.seed)
     g = to_device(inst, dev)
     p = binding.problem_for(inst, g["k"])
@@ -285,6 +291,87 @@ def main():
             cores = min(16, os.cpu_count() or 1)
         out["cpu_baseline"] = cpu_baseline(inst, args.cpu_rows, cores)
     print(json.dumps(out), flush=True)
+
+
+GATHER_ROW_BYTES = 1024      # one token's row in the pool (e.g. 512 bf16 values)
+
+
+def bench_gather(args, dev):
+    """li_gather of the decode workload's selection: 64 query rows x 2048 indices
+    into a paged pool of GATHER_ROW_BYTES-byte token rows (same block table)."""
+    inst = synth.make("decode", args.seed)
+    g = to_device(inst, dev)
+    p = binding.problem_for(inst, g["k"])
+    meta = binding.lightning_indexer_metadata(p, seqused_k=g["seqused_k"], device=dev)
+    idx, _ = binding.lightning_indexer(p, g["q"], g["k"], g["w"], metadata=meta,
+                                       seqused_k=g["seqused_k"], block_table=g["block_table"],
+                                       return_value=0)
+    idx = idx.reshape(-1, p.topk).contiguous()
+    rows, topk = idx.shape
+    R = GATHER_ROW_BYTES
+    gen = torch.Generator(device=dev).manual_seed(args.seed)
+    pool = torch.randint(0, 256, (inst["num_blocks"], inst["block_size"], R), dtype=torch.uint8,
+                         device=dev, generator=gen)
+    out = torch.empty((rows, topk, R), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    bt = g["block_table"]
+
+    def gather():
+        st = binding.li_gather(p, pool.data_ptr(), R, pool.stride(0), idx.data_ptr(), 1,
+                               bt.data_ptr(), meta.data_ptr(), out.data_ptr(), sh)
+        assert st == 0, binding.li_status_str(st)
+
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # read-evicts the caches
+    t_w = time.perf_counter()
+    done = 0
+    while done < args.warmup or time.perf_counter() - t_w < WARMUP_MIN_S:
+        flush.sum()
+        gather()
+        done += 1
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for s in range(args.steps):
+        flush.sum()
+        starts[s].record(stream)
+        gather()
+        ends[s].record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    t = float(np.mean(ms))
+    valid = int((idx >= 0).sum().item())
+    nbytes = valid * R + rows * topk * R + rows * topk * 4      # rows read, rows written, indices
+    achieved = nbytes / (t / 1000.0) / 1e9
+    out_json = {
+        "metric": "query-tokens/s (gather of the selected rows) and % of HBM bandwidth",
+        "value": rows / (t / 1000.0), "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "warmup_steps_run": done, "ms_per_step": t,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": "gather", "query_rows": rows, "topk": topk, "row_bytes": R,
+                   "select_block": 1, "layout_k": "PA_BSND", "block_size": inst["block_size"],
+                   "seed": args.seed},
+        "forward_ms": t, "forward_ms_p10": float(np.percentile(ms, 10)),
+        "forward_ms_p90": float(np.percentile(ms, 90)), "algorithmic_bytes": nbytes,
+        "selected_rows": valid,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic("gather")},
+    }
+    if not args.no_cpu_baseline:
+        from oracle.gather import gather as oracle_gather
+        sub = rows                                # every query row, timed on the host
+        kv = pool.cpu().numpy()
+        sub_inst = dict(inst, batch=sub, seqlens_q=inst["seqlens_q"][:sub],
+                        seqlens_k=inst["seqlens_k"][:sub])
+        t0 = time.perf_counter()
+        oracle_gather(sub_inst, kv, idx[:sub].cpu().numpy(), 1)
+        dt = time.perf_counter() - t0
+        out_json["cpu_baseline"] = {"value": sub / dt, "unit": "query-tokens/s", "cores": 1,
+                                    "kind": "oracle",
+                                    "sample": f"all {sub} query rows, plain Python/numpy "
+                                              f"gather; {dt:.2f} s wall"}
+    print(json.dumps(out_json), flush=True)
 
 
 if __name__ == "__main__":

@@ -176,6 +176,34 @@ li_status li_forward(const li_problem* p, const void* q, const void* k, const vo
                      const void* metadata, void* workspace, size_t workspace_bytes,
                      int32_t* sparse_indices, float* sparse_values, hipStream_t stream);
 
+/*
+ * Gathers, for every query row, the key (or value) rows its top-k selected: the
+ * step after the indexer, where sparse attention reads its selected keys
+ * (aclnnSparseFlashAttentionGrad page, calculation formula: the selected key is
+ * the gather of key by topkIndices[i] for i < selectBlockCount, each index a
+ * block of selectedBlockSize tokens).  One kernel on `stream`.
+ *  p            : the problem given to li_forward (layouts, lengths, topk, paged
+ *                 block size); its head counts and dtype are not used.
+ *  kv           : the token rows, row_bytes each (a multiple of 16; any element
+ *                 type), in the key layout of p: BSND [B, S2, row], TND [T2, row], or
+ *                 the paged pool [num_blocks, block_size, row] whose blocks are
+ *                 kv_block_stride bytes apart (0: block_size * row_bytes).
+ *  sparse_indices : int32 [rows, topk], as li_forward wrote them without an output
+ *                 index offset (sequence-local positions, -1 padding).
+ *  select_block : tokens per index (selectedBlockSize, >= 1): index i selects the
+ *                 tokens i * select_block .. i * select_block + select_block - 1.
+ *  block_table  : int32 [B, max_blocks_per_seq]; required iff layout_k == PA_BSND.
+ *  metadata     : filled by li_metadata for p.
+ *  out          : [rows, topk * select_block, row_bytes] bytes, 16-byte aligned.  An
+ *                 index of -1, or a token at or past the sequence's key count, gives a
+ *                 row of zero bytes.
+ * kv must be 16-byte aligned.
+ */
+li_status li_gather(const li_problem* p, const void* kv, int32_t row_bytes, int64_t kv_block_stride,
+                    const int32_t* sparse_indices, int32_t select_block,
+                    const int32_t* block_table, const void* metadata, void* out,
+                    hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* li_status_str(li_status s);
 

@@ -27,7 +27,8 @@ DTYPE = {torch.bfloat16: 0, torch.float8_e4m3fn: 1, torch.float32: 2, torch.floa
 STATUS = {0: "LI_OK", 1: "LI_ERR_INVALID_ARGUMENT", 2: "LI_ERR_UNSUPPORTED",
           3: "LI_ERR_WORKSPACE_TOO_SMALL", 4: "LI_ERR_HIP"}
 
-EXPORTED = ("li_metadata_size", "li_workspace_size", "li_metadata", "li_forward", "li_status_str")
+EXPORTED = ("li_metadata_size", "li_workspace_size", "li_metadata", "li_forward", "li_gather",
+            "li_status_str")
 
 
 class Problem(ctypes.Structure):
@@ -69,9 +70,12 @@ def load():
         L.li_metadata.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
         L.li_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                  vp, vp]
+        L.li_gather.argtypes = [P, vp, ctypes.c_int32, ctypes.c_int64, vp, ctypes.c_int32, vp, vp,
+                                vp, vp]
         L.li_status_str.argtypes = [ctypes.c_int]
         L.li_status_str.restype = ctypes.c_char_p
-        for n in ("li_metadata_size", "li_workspace_size", "li_metadata", "li_forward"):
+        for n in ("li_metadata_size", "li_workspace_size", "li_metadata", "li_forward",
+                  "li_gather"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -106,6 +110,12 @@ def li_forward(p: Problem, q, k, w, q_descale, k_descale, cu_seqlens_q, cu_seqle
                              cu_seqlens_k, seqused_k, cmp_residual_k, block_table,
                              output_idx_offset, metadata, workspace, workspace_bytes,
                              sparse_indices, sparse_values, stream)
+
+
+def li_gather(p: Problem, kv, row_bytes, kv_block_stride, sparse_indices, select_block,
+              block_table, metadata, out, stream) -> int:
+    return load().li_gather(ctypes.byref(p), kv, row_bytes, kv_block_stride, sparse_indices,
+                            select_block, block_table, metadata, out, stream)
 
 
 def li_status_str(status: int) -> str:
@@ -207,6 +217,24 @@ def lightning_indexer(p: Problem, q, k, w, *, metadata: torch.Tensor, q_descale=
                       metadata.data_ptr(), _ptr(workspace), wsb, idx.data_ptr(), _ptr(val),
                       stream), "li_forward")
     return idx, val
+
+
+def gather_selected(p: Problem, kv: torch.Tensor, sparse_indices: torch.Tensor, *,
+                    metadata: torch.Tensor, select_block: int = 1, block_table=None,
+                    out=None) -> torch.Tensor:
+    """Runs li_gather: the rows of `kv` (its last dimension holds one token's row,
+    the leading ones the key layout of `p`) that sparse_indices select.  Returns
+    uint8 [rows, topk * select_block, row_bytes] on the device."""
+    row_bytes = kv.shape[-1] * kv.element_size()
+    rows = sparse_indices.numel() // p.topk
+    stride = kv.stride(0) * kv.element_size() if p.layout_k == LAYOUT["PA_BSND"] else 0
+    if out is None:
+        out = torch.empty((rows, p.topk * select_block, row_bytes), dtype=torch.uint8,
+                          device=kv.device)
+    stream = torch.cuda.current_stream(kv.device).cuda_stream
+    _check(li_gather(p, kv.data_ptr(), row_bytes, stride, sparse_indices.data_ptr(), select_block,
+                     _ptr(block_table), metadata.data_ptr(), out.data_ptr(), stream), "li_gather")
+    return out
 
 
 def run_instance(inst: dict, device="cuda", return_value: int = 1):

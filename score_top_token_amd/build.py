@@ -16,7 +16,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblightning_indexer.so")
-SOURCES = ["li_host.cpp", "li_metadata.hip", "li_prefill.hip", "li_decode.hip"]
+SOURCES = ["li_host.cpp", "li_metadata.hip", "li_prefill.hip", "li_decode.hip", "li_gather.hip"]
 ARCH = os.environ.get("LI_OFFLOAD_ARCH", "gfx950")
 
 

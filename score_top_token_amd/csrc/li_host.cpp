@@ -304,6 +304,36 @@ li_status li_forward(const li_problem* p, const void* q, const void* k, const vo
   return e == hipSuccess ? LI_OK : LI_ERR_HIP;
 }
 
+li_status li_gather(const li_problem* p, const void* kv, int32_t row_bytes, int64_t kv_block_stride,
+                    const int32_t* sparse_indices, int32_t select_block,
+                    const int32_t* block_table, const void* metadata, void* out,
+                    hipStream_t stream) {
+  Plan pl;
+  li_status st = make_plan(p, &pl);
+  if (st != LI_OK) return st;
+  if (row_bytes <= 0 || row_bytes % 16 != 0 || select_block < 1) return LI_ERR_INVALID_ARGUMENT;
+  if ((p->layout_k == LI_LAYOUT_PA_BSND) != (block_table != nullptr)) return LI_ERR_INVALID_ARGUMENT;
+  if (!kv || !sparse_indices || !metadata || !out) return LI_ERR_INVALID_ARGUMENT;
+  if (!aligned(kv, 16) || !aligned(out, 16) || !aligned(sparse_indices, 4) || !aligned(metadata, 16))
+    return LI_ERR_INVALID_ARGUMENT;
+  int64_t stride = 0;
+  if (p->layout_k == LI_LAYOUT_PA_BSND) {
+    stride = kv_block_stride ? kv_block_stride : (int64_t)p->block_size * row_bytes;
+    if (stride < (int64_t)p->block_size * row_bytes || stride % 16 != 0) return LI_ERR_INVALID_ARGUMENT;
+  }
+  const int64_t rows = query_rows(p);
+  if (rows == 0) return LI_OK;
+  const int64_t per_row = (int64_t)p->topk * select_block;
+  if (per_row > INT32_MAX / 16 || rows * cdiv64(per_row, kGatherRows) > INT32_MAX)
+    return LI_ERR_UNSUPPORTED;
+  KArgs a = base_args(p, pl, const_cast<void*>(metadata));
+  a.k = kv;
+  a.block_table = block_table;
+  a.k_block_stride_bytes = stride;
+  const GatherArgs g{sparse_indices, static_cast<unsigned char*>(out), row_bytes, select_block};
+  return launch_gather(a, g, rows, stream) == hipSuccess ? LI_OK : LI_ERR_HIP;
+}
+
 const char* li_status_str(li_status s) {
   switch (s) {
     case LI_OK: return "LI_OK";

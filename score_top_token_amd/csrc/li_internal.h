@@ -108,8 +108,18 @@ enum { L_BSND = 0, L_TND = 1, L_PA = 2 };
 enum { KL_CONTIG = 0, KL_PAGED = 1, KL_PAGED_TILE = 2 };
 enum { DT_BF16 = 0, DT_FP8 = 1, DT_FP32 = 2, DT_FP16 = 3 };
 
+// li_gather: the selected rows' source and destination.
+struct GatherArgs {
+  const int32_t* idx;       // sparse_indices [rows, topk]
+  unsigned char* out;       // [rows, topk * sel, row_bytes]
+  int32_t row_bytes;        // bytes per token row, a multiple of 16
+  int32_t sel;              // tokens per selected index
+};
+constexpr int kGatherRows = 64;          // selected rows per gather workgroup
+
 // Launchers (defined in the .hip files); return the hipGetLastError() of the launch.
 hipError_t launch_metadata(const KArgs& a, int mode, hipStream_t s);
+hipError_t launch_gather(const KArgs& a, const GatherArgs& g, int64_t rows, hipStream_t s);
 hipError_t launch_prefill(const KArgs& a, int mode, int qk_dtype, int w_dtype, int mblocks,
                           int kl, int grid, size_t lds, hipStream_t s);
 hipError_t launch_decode(const KArgs& a, int qk_dtype, int w_dtype, int mblocks, int kl,

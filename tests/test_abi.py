@@ -180,3 +180,26 @@ def test_problem_struct_matches_header():
             decl += [n.strip() for n in m.group(2).split(",")]
     assert [f[0] for f in binding.Problem._fields_] == decl
     assert ctypes.sizeof(binding.Problem) == 18 * 4 + 8
+
+
+def test_gather_pointer_rules():
+    p = base_problem()
+    _, mb = binding.li_metadata_size(p)
+    F = FAKE
+
+    def call(prob=p, kv=F, rb=64, stride=0, idx=F, sel=1, bt=None, meta=F, out=F):
+        return binding.li_gather(prob, kv, rb, stride, idx, sel, bt, meta, out, None)
+
+    assert call(rb=0) == INVALID                           # row bytes > 0
+    assert call(rb=40) == INVALID                          # multiple of 16
+    assert call(sel=0) == INVALID                          # select block >= 1
+    assert call(kv=None) == INVALID
+    assert call(idx=None) == INVALID
+    assert call(meta=None) == INVALID
+    assert call(out=None) == INVALID
+    assert call(kv=F + 8) == INVALID                       # 16-byte alignment
+    assert call(bt=F) == INVALID                           # block_table only with PA
+    pa = pa_problem()
+    assert call(prob=pa) == INVALID                        # PA needs block_table
+    assert call(prob=pa, bt=F, stride=16) == INVALID       # stride below a block
+    assert call(prob=base_problem(batch=0)) == OK          # nothing to gather
