@@ -30,8 +30,11 @@ constexpr int kDecodeDepth = 4;   // 32-key tiles in flight per wave (even)
 // kDecodeDepth * 32 keys are in flight per wave.  Each tile passes through the
 // wave's own LDS buffer to reach the MFMA operand layout; its MFMAs are
 // interleaved with the epilogue of the previous tile.
+// One wave per SIMD by design (a 4-deep register ring of 32-key tiles): the
+// attribute keeps the compiler from trading that ring for occupancy.
 template <int QK, int MB, int WT, int KL>
-__global__ __launch_bounds__(kDecodeWaves * 64, 1) void split_kernel(KArgs a) {
+__global__ __launch_bounds__(kDecodeWaves * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void split_kernel(KArgs a) {
   typedef Mma<QK> M;
   typedef typename M::frag F;
   constexpr int D = kDecodeDepth;
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 1) void split_kernel(KArgs a) {
   // Step t (ring set S = t % D): tile t from set S into LDS, refill set S with
   // tile t + D, MFMAs of tile t into one accumulator set interleaved with the
   // epilogue of tile t - 1 from the other.
-  auto step = [&](auto set, int t) {
+  auto step = [&](auto set, int t) __attribute__((always_inline)) {
     constexpr int S = decltype(set)::value;
     f32x16(&cur)[MB] = (S & 1) ? accB : accA;
     f32x16(&prev)[MB] = (S & 1) ? accA : accB;

@@ -64,19 +64,22 @@ __device__ inline float block_score(const f32x16 (&acc)[MB], const float (&wv)[M
 
 // Interleave hint for one pipelined iteration: each MFMA is followed by a few
 // VALU instructions of the previous tile's epilogue.
-template <int QK, int MB>
+template <int QK, int MB, bool kReadsFirst = true>
 __device__ inline void pipe_schedule() {
   constexpr int NMFMA = MB * Mma<QK>::KSTEPS;
   constexpr int NVALU = MB * 32 + 8;
   constexpr int PER = (NVALU + NMFMA - 1) / NMFMA;
   constexpr int NREAD = Mma<QK>::KSTEPS * Mma<QK>::FB / 16;
-  // fragment reads of the first half of the k-steps, their MFMAs (each followed
-  // by VALU work), then the second half: half the fragment registers suffice
+  // every fragment read first (they queue in the LDS together, behind no MFMA),
+  // then the MFMAs, each followed by VALU work of the epilogue; with
+  // kReadsFirst = false the reads of the second half of the k-steps wait for the
+  // first half's MFMAs, so half the fragment registers suffice
+  constexpr int H = kReadsFirst ? 1 : 2;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    __builtin_amdgcn_sched_group_barrier(0x100, NREAD / 2, 0);
+  for (int h = 0; h < H; ++h) {
+    __builtin_amdgcn_sched_group_barrier(0x100, NREAD / H, 0);
 #pragma unroll
-    for (int i = 0; i < NMFMA / 2; ++i) {
+    for (int i = 0; i < NMFMA / H; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, PER, 0); // then VALU work
     }

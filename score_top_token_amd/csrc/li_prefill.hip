@@ -213,7 +213,7 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
   // epilogue of tile t-1 from `prev`, then tile t-2's scores are written: they
   // are a step old, so the write never waits on the epilogue's latency.
   float pend = 0.0f;                       // descaled scores of tile t-1, not yet written
-  auto step = [&](auto set, int t, f32x16 (&cur)[MB], const f32x16 (&prev)[MB]) {
+  auto step = [&](auto set, int t, f32x16 (&cur)[MB], const f32x16 (&prev)[MB]) __attribute__((always_inline)) {
     constexpr int S = decltype(set)::value;
     // set S (tile t) went to LDS in the previous step: refill it first, so
     // the wait for tile t+1 below leaves D-1 tiles in flight
@@ -227,7 +227,8 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
     const float ds = QK == DT_FP8 ? dsc_lds[((t - 1) & (kDscSlots - 1)) * 32 + (lane & 31)] : 1.0f;
     mma_tile<QK, MB>(qf, kb, cur);
     const float prev_score = block_score<MB>(prev, wv);
-    pipe_schedule<QK, MB>();
+    // the per-key paged addressing leaves no room for every fragment at once
+    pipe_schedule<QK, MB, KL != KL_PAGED>();
     if (t > 1) emit(t - 2, pend);
     pend = QK == DT_FP8 ? prev_score * ds : prev_score;
     __syncthreads();

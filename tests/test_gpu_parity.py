@@ -182,6 +182,10 @@ SMALL = {
                                        qk_dtype="fp8", w_scale=0.25)),
     "stream_long_k8192": (None, 38, dict(batch=1, s1=5, s2=265000, n1=8, topk=8192,
                                          qk_dtype="fp16", w_dtype="fp32")),
+    # 64 heads with a paged block size that is not a multiple of 32 (per-key lookups)
+    "decode_paged_bs16_h64": (None, 39, dict(batch=3, s1=1, n1=64, topk=100, layout_k="PA_BSND",
+                                             len_lo=100, len_hi=2000, block_size=16,
+                                             w_scale=0.125)),
     "idx_offset_decode": (None, 35, dict(batch=6, s1=1, n1=64, topk=200, layout_k="PA_BSND",
                                          len_lo=100, len_hi=4000, block_size=128,
                                          idx_offset_max=1 << 20, w_scale=0.125)),
