@@ -86,21 +86,56 @@ __device__ inline float load_w(const void* w, int64_t idx) {
   }
 }
 
+// LDS bytes one wave needs to stage a 32-head block of its query row.
+template <int QK>
+constexpr int q_stage_bytes() { return 32 * Mma<QK>::RB; }
+
 // Q fragments (MFMA A operand) and per-lane weights of one query row.  Heads at or
 // above n1 get zero q and zero weight, so they add nothing.
-template <int QK, int MB, int WT>
+// A fragment load has each lane read 16 bytes of a different head row, so one
+// instruction touches 64 cache lines for 1 KiB.  With kStaged the wave instead
+// reads each 32-head block with 1 KiB-contiguous loads, parks it in its own
+// q_stage_bytes() of LDS at `stage` (the K tiles' XOR swizzle, so the fragment
+// reads spread over the banks) and reads the fragments back from there.
+template <int QK, int MB, int WT, bool kStaged = false>
 __device__ inline void load_query(const KArgs& a, int64_t tok, int lane,
                                   typename Mma<QK>::frag (&qf)[MB][Mma<QK>::KSTEPS],
-                                  float (&wv)[MB][16]) {
+                                  float (&wv)[MB][16], unsigned char* stage = nullptr) {
   typedef Mma<QK> M;
   const unsigned char* qrow = reinterpret_cast<const unsigned char*>(a.q) + tok * a.n1 * M::RB;
+  if constexpr (kStaged) {
+    constexpr int NCH = M::RB / 16;            // 16-byte chunks per head row
+    constexpr int NLD = 32 * NCH / 64;         // chunks per lane per block: 8 (bf16), 4 (fp8)
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int head = mb * 32 + (lane & 31);
+    for (int mb = 0; mb < MB; ++mb) {
+      i32x4 v[NLD];
 #pragma unroll
-    for (int j = 0; j < M::KSTEPS; ++j)
-      qf[mb][j] = head < a.n1 ? load_frag_global<QK>(qrow + head * M::RB + frag_off<QK>(lane, j))
-                              : zero_frag<QK>();
+      for (int r = 0; r < NLD; ++r) {
+        const int id = r * 64 + lane, hl = id / NCH, c = id % NCH;
+        const int head = mb * 32 + hl;
+        const bool in = head < a.n1;
+        v[r] = *reinterpret_cast<const i32x4*>(qrow + (int64_t)(in ? head : a.n1 - 1) * M::RB + c * 16);
+        if (!in) v[r] = i32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int r = 0; r < NLD; ++r) {
+        const int id = r * 64 + lane;
+        *reinterpret_cast<i32x4*>(stage + lds_chunk_off<QK>(id / NCH, id % NCH)) = v[r];
+      }
+      wave_sync();
+#pragma unroll
+      for (int j = 0; j < M::KSTEPS; ++j) qf[mb][j] = load_frag_lds<QK>(stage, lane & 31, lane, j);
+      wave_sync();                               // the next block's stores follow these reads
+    }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int head = mb * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < M::KSTEPS; ++j)
+        qf[mb][j] = head < a.n1 ? load_frag_global<QK>(qrow + head * M::RB + frag_off<QK>(lane, j))
+                                : zero_frag<QK>();
+    }
   }
   const float qd = (QK == DT_FP8) ? a.q_descale[tok] : 1.0f;
   // Accumulator rows 4g .. 4g+3 of a lane are 4 consecutive heads h0 .. h0+3

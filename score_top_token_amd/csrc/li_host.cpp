@@ -90,7 +90,10 @@ li_status make_plan(const li_problem* p, Plan* pl) {
   // per-wave select scratch, whichever is larger; then the score rows
   const size_t tiles = 2 * (size_t)kPipeKeys * rb + (p->qk_dtype == LI_DT_FP8_E4M3 ? 4 * 32 * 4 : 0);
   const size_t dense_r0 = std::max(tiles, (size_t)kDenseWaves * kDenseScratch);
-  const size_t dense_lds = dense_r0 + (size_t)kDenseWaves * dcap * 4;
+  // before the score loop each wave stages a 32-head block of its query in the
+  // same space
+  const size_t q_stage = (size_t)kDenseWaves * 32 * rb;
+  const size_t dense_lds = std::max(dense_r0 + (size_t)kDenseWaves * dcap * 4, q_stage);
   int64_t items;
   if (use_decode(p)) {
     pl->mode = kModeDecode;
@@ -119,7 +122,7 @@ li_status make_plan(const li_problem* p, Plan* pl) {
     pl->grid = (int32_t)std::min<int64_t>(items, kDenseSlots);
     pl->ws_row_stride = dcap;
     pl->ws_bytes = (size_t)pl->grid * kDenseWaves * dcap * 4;
-    pl->lds_prefill = std::max(tiles, (size_t)kDenseWaves * kWideScratch);
+    pl->lds_prefill = std::max(std::max(tiles, (size_t)kDenseWaves * kWideScratch), q_stage);
   } else {
     // rows past the workspace cap (over 262144 keys): bounded candidate lists
     pl->mode = kModeStream;

@@ -164,9 +164,12 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
   st.prefetch_table(a, b, 0);
   F qf[MB][M::KSTEPS];
   float wv[MB][16];
-  if (has_row) load_query<QK, MB, WT>(a, tok, lane, qf, wv);
+  // the query goes through LDS (coalesced loads); each wave's staging area
+  // overlaps the K tiles and the rows, so all waves finish with it first
+  if (has_row) load_query<QK, MB, WT, true>(a, tok, lane, qf, wv, smem + wave * q_stage_bytes<QK>());
   else zero_query<QK, MB>(qf, wv);
   settle_loads();
+  __syncthreads();
 
   // results of tile t (descaled): lanes 0-31 carry keys t*32 + lane, lanes
   // 32-63 the same scores again.  Every row's scores go to its row (the rows
@@ -225,10 +228,12 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
     st.template store<(S + 1) % D>(smem + ((t + 1) & 1) * TILE, tid);
     st.template store_dsc<(S + 1) % D>(dsc_lds + ((t + 1) & (kDscSlots - 1)) * 32, tid);
     const float ds = QK == DT_FP8 ? dsc_lds[((t - 1) & (kDscSlots - 1)) * 32 + (lane & 31)] : 1.0f;
+    __builtin_amdgcn_s_setprio(2);
     mma_tile<QK, MB>(qf, kb, cur);
     const float prev_score = block_score<MB>(prev, wv);
     // the per-key paged addressing leaves no room for every fragment at once
     pipe_schedule<QK, MB, KL != KL_PAGED>();
+    __builtin_amdgcn_s_setprio(1);
     if (t > 1) emit(t - 2, pend);
     pend = QK == DT_FP8 ? prev_score * ds : prev_score;
     __syncthreads();
@@ -236,7 +241,12 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
   // Full groups of 4 steps (two accumulator sets x ring) run unconditionally, so
   // every step issues the same loads and the waits stay static counts; the last
   // 0-3 tiles follow.
+  // Issue priority: a wave in its MFMA stretch first (2), then a wave in the
+  // score loop (1), then a wave loading its query or selecting (0).  The SIMD's
+  // other wave, from the other workgroup on the CU, is often in a different
+  // phase; this keeps the matrix core fed from whichever wave has MFMAs ready.
   int t = 0;
+  __builtin_amdgcn_s_setprio(1);
   for (; t + 4 <= ntiles; t += 4) {
     step(IntC<0>(), t, accA, accB);
     step(IntC<1>(), t + 1, accB, accA);
@@ -254,6 +264,7 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
     emit(last, QK == DT_FP8 ? sc * ds : sc);
   }
   __syncthreads();                         // the tile area becomes select scratch
+  __builtin_amdgcn_s_setprio(0);
   if (!has_row) return;
   if (direct) {
     // every visible key is kept: the row in key order, then the padding
