@@ -285,7 +285,7 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
   if constexpr (G) {
     uint32_t* hist = reinterpret_cast<uint32_t*>(smem + wave * kWideScratch);
     uint32_t* scr = hist + kWideBuckets;
-    if (!wave_topk_row<kWideBuckets>(row, lim, topk, lo, hi, hist, scr, oi, ov, ioff)) {
+    if (!wave_topk_row_call<kWideBuckets>(row, lim, topk, lo, hi, hist, scr, oi, ov, ioff)) {
       wave_kth(row, nullptr, lim, topk, lo, hi, scr + 2 * kSelSmall, scr, fb, eb);
       write_kept_row(row, lim, fb, eb, oi, ov, topk, ioff);
     }

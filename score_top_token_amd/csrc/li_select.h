@@ -329,7 +329,7 @@ __device__ inline void wave_find_bucket_n(const uint32_t* hist, int r, int& bkt,
 // holds more than kSelSmall entries.  hist: NB u32 and scr: 2 * kSelSmall
 // words of LDS private to the wave.
 template <int NB>
-__device__ inline bool wave_topk_row(const float* vals, int n, int k, float lo, float hi,
+__device__ __forceinline__ bool wave_topk_row(const float* vals, int n, int k, float lo, float hi,
                                      uint32_t* hist, uint32_t* scr, int32_t* oi, float* ov,
                                      int ioff) {
   if (!(lo < hi)) return false;
@@ -388,6 +388,16 @@ __device__ inline bool wave_topk_row(const float* vals, int n, int k, float lo, 
     if (ov) ov[o] = cf;
   }
   return true;
+}
+
+// The same, out of line: where the score loop already holds most registers
+// (rows in a global workspace), a call keeps the select's registers out of
+// the loop's allocation.
+template <int NB>
+__device__ __noinline__ bool wave_topk_row_call(const float* vals, int n, int k, float lo, float hi,
+                                                uint32_t* hist, uint32_t* scr, int32_t* oi,
+                                                float* ov, int ioff) {
+  return wave_topk_row<NB>(vals, n, k, lo, hi, hist, scr, oi, ov, ioff);
 }
 
 }  // namespace li
