@@ -53,12 +53,14 @@ __device__ inline void mma_tile(const typename Mma<QK>::frag (&qf)[MB][Mma<QK>::
 // the score of key l % 32.
 template <int MB>
 __device__ inline float block_score(const f32x16 (&acc)[MB], const float (&wv)[MB][16]) {
-  float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // one chain of fused multiply-adds: a wave64 VALU op takes four issue cycles,
+  // which covers its latency, so the chain costs no more than split partial sums
+  // and saves their final adds
+  float s = 0.0f;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) p[r & 3] = fmaf(wv[mb][r], relu(acc[mb][r]), p[r & 3]);
-  const float s = (p[0] + p[1]) + (p[2] + p[3]);
+    for (int r = 0; r < 16; ++r) s = fmaf(wv[mb][r], relu(acc[mb][r]), s);
   return s + __shfl_xor(s, 32);
 }
 
@@ -98,13 +100,16 @@ __device__ inline void pipe_schedule() {
 // reports (dsc[S]), loaded right behind the tile so that waiting for it never
 // drains the loads of later tiles; the workgroup kernels pass it on through an
 // LDS slot per tile (kDscSlots slots of 32 floats).
-template <int QK, int KL, int NT, int D>
+// kClampOffset: a partial tile clamps the lanes' byte offsets (one min per
+// load) rather than their keys (a min and a select per load).
+template <int QK, int KL, int NT, int D, bool kClampOffset = false>
 struct PipeStage {
   static constexpr int RB = Mma<QK>::RB;
   static constexpr int NCH = RB / 16;
   static constexpr int CHUNKS = kPipeKeys * NCH;
   static constexpr int LOADS = (CHUNKS + NT - 1) / NT;
   static_assert(CHUNKS % NT == 0, "a tile is an exact number of chunks per thread");
+  static_assert(NT % NCH == 0, "a thread loads the same chunk column of each of its rows");
   i32x4 pre[D][LOADS];
   float dsc[D];
   // KL_PAGED_TILE: the physical ids of 64 consecutive logical blocks from
@@ -170,13 +175,26 @@ struct PipeStage {
         tile = reinterpret_cast<const unsigned char*>(a.k) + ((int64_t)k_off + base) * RB;
         slot0 = (int64_t)k_off + base;
       }
+      if constexpr (kClampOffset) {
+        // byte offset of the lane's chunk, clamped to row `last`: the offset is
+        // monotonic in the key, so clamping it clamps the key (a no-op for a
+        // full tile); the bound is shared by the lane's loads (NT % NCH == 0)
+        const uint32_t bound = (uint32_t)(last * RB + (tid % NCH) * 16);
 #pragma unroll
-      for (int r = 0; r < LOADS; ++r) {
-        const int id = tid + NT * r;
-        int key = id / NCH;
-        const int c = id % NCH;
-        if (!full) key = key < last ? key : last;
-        pre[S][r] = *reinterpret_cast<const i32x4*>(tile + (uint32_t)(key * RB + c * 16));
+        for (int r = 0; r < LOADS; ++r) {
+          const int id = tid + NT * r;
+          const uint32_t off = (uint32_t)((id / NCH) * RB + (id % NCH) * 16);
+          pre[S][r] = *reinterpret_cast<const i32x4*>(tile + (off < bound ? off : bound));
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < LOADS; ++r) {
+          const int id = tid + NT * r;
+          int key = id / NCH;
+          const int c = id % NCH;
+          if (!full) key = key < last ? key : last;
+          pre[S][r] = *reinterpret_cast<const i32x4*>(tile + (uint32_t)(key * RB + c * 16));
+        }
       }
       if constexpr (QK == DT_FP8) {
         const int key = (tid & 31) < last ? (tid & 31) : last;

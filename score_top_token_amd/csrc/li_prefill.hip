@@ -33,6 +33,10 @@ __device__ inline float canon(float f) {
   if (f == 0.0f) return 0.0f;
   return f != f ? -__builtin_inff() : f;
 }
+// The same in two VALU ops instead of four: f is an arithmetic result, so a
+// NaN is quiet and max(f, -inf) returns -inf for it; adding +0 then turns -0
+// into +0 (round to nearest).
+__device__ inline float canon2(float f) { return __builtin_fmaxf(f, -__builtin_inff()) + 0.0f; }
 
 // Writes the top-k of a score row in ascending key order, given its k-th element.
 // vals: LDS scores; idx: LDS keys or nullptr (key = position).  At most topk
@@ -160,7 +164,7 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
 
   // fp8 tiles are half the registers: four in flight hide more of the L2 / MALL latency
   constexpr int D = QK == DT_FP8 ? 4 : kStageDepth;
-  PipeStage<QK, KL, NT, D> st;
+  PipeStage<QK, KL, NT, D, G> st;
   st.prefetch_table(a, b, 0);
   F qf[MB][M::KSTEPS];
   float wv[MB][16];
@@ -181,7 +185,9 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
   auto emit = [&](int t, float tot) {
     const int s = t * kPipeKeys + (lane & 31);
     const bool in = lane < 32 && s < lim;
-    const float f = canon(tot);
+    // Fewer VALU ops pay off where the rows live in global memory; with LDS
+    // rows (up to 4096 keys) the longer forms measure faster (schedule effect).
+    const float f = G ? canon2(tot) : canon(tot);
     if constexpr (G) {
       // every lane stores (lanes 32-63 repeat lanes 0-31); keys past lim land
       // below the row stride, in slots that are never read
@@ -189,8 +195,14 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
     } else {
       if (in) row[s] = f;
     }
-    vmin = in ? fminf(vmin, f) : vmin;
-    vmax = in ? fmaxf(vmax, f) : vmax;
+    if constexpr (G) {
+      // f is never NaN: a compare and a select each, no operand quieting
+      vmin = (in & (f < vmin)) ? f : vmin;
+      vmax = (in & (f > vmax)) ? f : vmax;
+    } else {
+      vmin = in ? fminf(vmin, f) : vmin;
+      vmax = in ? fmaxf(vmax, f) : vmax;
+    }
   };
 
   f32x16 accA[MB], accB[MB];
