@@ -17,6 +17,8 @@
 // Values are never NaN; -0 has been folded into +0 by the producer.
 #pragma once
 
+#include <type_traits>
+
 #include "li_device.h"
 
 namespace li {
@@ -251,17 +253,21 @@ constexpr int kRowUnroll = 16;
 constexpr int kWideBuckets = 2048;
 constexpr int kLdsBuckets = 512;
 
-// Linear value bucket in [0, NB); halving first keeps (hi - lo) finite.
+// Linear value bucket in [0, NB): one fused multiply-add, a median-of-three
+// clamp and a conversion, each monotone in f, so a key of a higher bucket is
+// never below a key of a lower one.  Halving first keeps (hi - lo) finite; for f
+// in [lo, hi] the product f * a stays within a few units of NB * 2^24.
 template <int NB>
 struct FBucketN {
-  float lo2, scale;
+  float a, c;
   __device__ FBucketN(float lo, float hi) {
-    lo2 = lo * 0.5f;
-    scale = fminf((float)NB / (hi * 0.5f - lo2), 3.0e38f);
+    const float lo2 = lo * 0.5f;
+    const float scale = fminf((float)NB / (hi * 0.5f - lo2), 3.0e38f);
+    a = 0.5f * scale;
+    c = -lo2 * scale;
   }
   __device__ uint32_t operator()(float f) const {
-    const float x = fminf((f * 0.5f - lo2) * scale, (float)(NB - 1));
-    return (uint32_t)fmaxf(x, 0.0f);
+    return (uint32_t)__builtin_amdgcn_fmed3f(fmaf(f, a, c), 0.0f, (float)(NB - 1));
   }
 };
 
@@ -348,29 +354,34 @@ __device__ __forceinline__ bool wave_topk_row(const float* vals, int n, int k, f
   float* sf = reinterpret_cast<float*>(scr);
   uint32_t* se = scr + kSelSmall;
   int pos = 0, got = 0;
-  row_pass(vals, n, [&](int p, bool valid, float f) __attribute__((always_inline)) {
-    const uint32_t bk = fbk(f);
-    const bool up = valid && bk > (uint32_t)B;
-    const uint64_t mu = ballot(up);
-    if (up) {
+  // one predicated store region per entry (the values array's presence is a
+  // compile-time branch); bucket B is rare, so its gathering sits behind a
+  // uniform test of its ballot
+  auto pass2 = [&](auto has_ov) __attribute__((always_inline)) {
+    row_pass(vals, n, [&](int p, bool valid, float f) __attribute__((always_inline)) {
+      const uint32_t bk = fbk(f);
+      const bool up = valid & (bk > (uint32_t)B);
+      const uint64_t mu = ballot(up);
       const int o = pos + mbcnt(mu);
-      if (o < k) {
+      if (up & (o < k)) {
         oi[o] = p + ioff;
-        if (ov) ov[o] = f;
+        if constexpr (decltype(has_ov)::value) ov[o] = f;
       }
-    }
-    pos += __popcll(mu);
-    const bool take = valid && bk == (uint32_t)B;
-    const uint64_t mt = ballot(take);
-    if (take) {
-      const int slot = got + mbcnt(mt);
-      if (slot < kSelSmall) {
-        sf[slot] = f;
-        se[slot] = (uint32_t)p;
+      pos += __popcll(mu);
+      const bool take = valid & (bk == (uint32_t)B);
+      const uint64_t mt = ballot(take);
+      if (mt != 0) {
+        const int slot = got + mbcnt(mt);
+        if (take & (slot < kSelSmall)) {
+          sf[slot] = f;
+          se[slot] = (uint32_t)p;
+        }
+        got += __popcll(mt);
       }
-    }
-    got += __popcll(mt);
-  });
+    });
+  };
+  if (ov) pass2(std::true_type{});
+  else pass2(std::false_type{});
   wave_sync();
   const int m = got < kSelSmall ? got : kSelSmall;
   const float cf = l < m ? sf[l] : 0.0f;
