@@ -315,15 +315,18 @@ __device__ inline void block_find_bucket(SelShared& sh, int r) {
   __syncthreads();
 }
 
+// linear value bucket in [0, kNB), monotone in f (one fused multiply-add, a
+// median-of-three clamp and a conversion)
 struct FBucketN {
-  float lo2, scale;
+  float a, c;
   __device__ FBucketN(float lo, float hi) {
-    lo2 = lo * 0.5f;
-    scale = fminf((float)kNB / (hi * 0.5f - lo2), 3.0e38f);
+    const float lo2 = lo * 0.5f;
+    const float scale = fminf((float)kNB / (hi * 0.5f - lo2), 3.0e38f);
+    a = 0.5f * scale;
+    c = -lo2 * scale;
   }
   __device__ uint32_t operator()(float f) const {
-    const float x = fminf((f * 0.5f - lo2) * scale, (float)(kNB - 1));
-    return (uint32_t)fmaxf(x, 0.0f);
+    return (uint32_t)__builtin_amdgcn_fmed3f(fmaf(f, a, c), 0.0f, (float)(kNB - 1));
   }
 };
 
