@@ -1,7 +1,7 @@
 """Python access to the plain CPU oracle (oracle/li_oracle.c).
 
 TEST INFRASTRUCTURE ONLY: tests/, the smoke check and the bench's CPU-baseline
-leg use it to judge the HIP library.  The product package never imports it.
+leg use it to check the HIP library against.  The product package never imports it.
 
 `build()` compiles li_oracle.c with gcc into oracle/liboracle.so; the other
 functions take a problem instance as produced by score_top_token_amd.synth.make

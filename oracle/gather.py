@@ -1,7 +1,7 @@
 """Plain CPU gather of the rows that sparse_indices select (oracle of li_gather).
 
 TEST INFRASTRUCTURE ONLY: tests/, the smoke check and the bench's CPU-baseline
-leg use it to judge the HIP library; the product package never imports it.
+leg use it to check the HIP library against; the product package never imports it.
 
 Follows the aclnnSparseFlashAttentionGrad page, calculation formula: the
 selected key (and value) is the gather of key (value) by topkIndices[i] for

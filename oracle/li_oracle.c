@@ -2,7 +2,7 @@
  * Plain CPU oracle of the Lightning Indexer forward pass.
  *
  * TEST INFRASTRUCTURE ONLY: used by tests/, the smoke check and the bench's CPU
- * baseline to judge the HIP library.  Never linked into the product.
+ * baseline to check the HIP library against.  Never linked into the product.
  *
  * Each step follows the pages directly, with no tiling, blocking, radix or
  * histogram tricks:
