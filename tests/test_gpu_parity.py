@@ -189,6 +189,13 @@ SMALL = {
     "idx_offset_decode": (None, 35, dict(batch=6, s1=1, n1=64, topk=200, layout_k="PA_BSND",
                                          len_lo=100, len_hi=4000, block_size=128,
                                          idx_offset_max=1 << 20, w_scale=0.125)),
+    # score magnitudes far from 1 (weights scaled by 1e-30 or 1e25): the selects'
+    # linear bucket maps over [row minimum, row maximum] at both ends of the range
+    "scores_tiny_lds": (None, 40, dict(batch=1, s1=600, s2=600, n1=16, topk=100, w_scale=1e-30)),
+    "scores_huge_lds": (None, 41, dict(batch=1, s1=600, s2=600, n1=16, topk=100, w_scale=1e25)),
+    "scores_huge_global": (None, 42, dict(batch=1, s1=20, s2=6000, n1=16, topk=300, w_scale=1e25)),
+    "scores_huge_decode": (None, 43, dict(batch=3, s1=1, n1=16, topk=100, layout_k="PA_BSND",
+                                          len_lo=500, len_hi=3000, block_size=64, w_scale=1e25)),
 }
 
 
