@@ -189,6 +189,14 @@ SMALL = {
     "idx_offset_decode": (None, 35, dict(batch=6, s1=1, n1=64, topk=200, layout_k="PA_BSND",
                                          len_lo=100, len_hi=4000, block_size=128,
                                          idx_offset_max=1 << 20, w_scale=0.125)),
+    # fp8 keys with rows in the workspace (tiles through LDS in pairs): odd and even
+    # tile counts, and TND items of 1-2 tiles next to long ones
+    "fp8_global_rows_odd": (None, 44, dict(batch=1, s1=70, s2=7000, n1=64, topk=300,
+                                           qk_dtype="fp8", w_scale=0.125)),
+    "fp8_global_rows_even_mask0": (None, 45, dict(batch=1, s1=37, s2=6016, n1=32, topk=500,
+                                                  qk_dtype="fp8", mask_mode=0)),
+    "fp8_global_tnd": (None, 46, dict(batch=4, n1=16, topk=64, layout_q="TND", layout_k="TND",
+                                      len_lo=20, len_hi=6500, qk_dtype="fp8")),
     # score magnitudes far from 1 (weights scaled by 1e-30 or 1e25): the selects'
     # linear bucket maps over [row minimum, row maximum] at both ends of the range
     "scores_tiny_lds": (None, 40, dict(batch=1, s1=600, s2=600, n1=16, topk=100, w_scale=1e-30)),
