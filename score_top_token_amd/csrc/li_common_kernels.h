@@ -97,30 +97,39 @@ constexpr int q_stage_bytes() { return 32 * Mma<QK>::RB; }
 // reads each 32-head block with 1 KiB-contiguous loads, parks it in its own
 // q_stage_bytes() of LDS at `stage` (the K tiles' XOR swizzle, so the fragment
 // reads spread over the banks) and reads the fragments back from there.
-template <int QK, int MB, int WT, bool kStaged = false>
+// `mid()` runs in the staged path once the query's loads are issued and before
+// they are waited for, so that loads it issues queue behind them.
+struct NoMid {
+  __device__ void operator()() const {}
+};
+template <int QK, int MB, int WT, bool kStaged = false, class Mid = NoMid>
 __device__ inline void load_query(const KArgs& a, int64_t tok, int lane,
                                   typename Mma<QK>::frag (&qf)[MB][Mma<QK>::KSTEPS],
-                                  float (&wv)[MB][16], unsigned char* stage = nullptr) {
+                                  float (&wv)[MB][16], unsigned char* stage = nullptr,
+                                  Mid mid = Mid()) {
   typedef Mma<QK> M;
   const unsigned char* qrow = reinterpret_cast<const unsigned char*>(a.q) + tok * a.n1 * M::RB;
   if constexpr (kStaged) {
     constexpr int NCH = M::RB / 16;            // 16-byte chunks per head row
     constexpr int NLD = 32 * NCH / 64;         // chunks per lane per block: 8 (bf16), 4 (fp8)
+    i32x4 v[MB][NLD];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      i32x4 v[NLD];
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < NLD; ++r) {
         const int id = r * 64 + lane, hl = id / NCH, c = id % NCH;
         const int head = mb * 32 + hl;
         const bool in = head < a.n1;
-        v[r] = *reinterpret_cast<const i32x4*>(qrow + (int64_t)(in ? head : a.n1 - 1) * M::RB + c * 16);
-        if (!in) v[r] = i32x4{0, 0, 0, 0};
+        v[mb][r] = *reinterpret_cast<const i32x4*>(qrow + (int64_t)(in ? head : a.n1 - 1) * M::RB + c * 16);
+        if (!in) v[mb][r] = i32x4{0, 0, 0, 0};
       }
+    mid();
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int r = 0; r < NLD; ++r) {
         const int id = r * 64 + lane;
-        *reinterpret_cast<i32x4*>(stage + lds_chunk_off<QK>(id / NCH, id % NCH)) = v[r];
+        *reinterpret_cast<i32x4*>(stage + lds_chunk_off<QK>(id / NCH, id % NCH)) = v[mb][r];
       }
       wave_sync();
 #pragma unroll

@@ -50,12 +50,21 @@ void split_kernel(KArgs a) {
   const int4 br = batch_rec(a, b);
   const int64_t tok = (int64_t)br.x + i;
   unsigned char* tile = smem + wave * TILE;
+  static_assert(q_stage_bytes<QK>() <= TILE, "a 32-head query block fits the wave's tile");
 
   PipeStage<QK, KL, 64, D> st;
   st.prefetch_table(a, b, k0);
   F qf[MB][M::KSTEPS];
   float wv[MB][16];
-  load_query<QK, MB, WT>(a, tok, lane, qf, wv);
+  // the query goes through the wave's LDS tile (coalesced loads), with the K
+  // ring's first loads issued behind its loads
+  auto fill_ring = [&]() __attribute__((always_inline)) {
+    static_for<D>([&](auto set) {
+      constexpr int S = decltype(set)::value;
+      st.template load<S>(a, b, br.z, k0 + S * kPipeKeys, k1, lane);
+    });
+  };
+  load_query<QK, MB, WT, true>(a, tok, lane, qf, wv, tile, fill_ring);
   float* dst = a.ws + ((int64_t)b * a.s1max + i) * a.ws_row_stride;
 
   // score of tile t: lanes 0-31 carry keys k0 + 32 t + lane.  The segment's
@@ -81,10 +90,6 @@ void split_kernel(KArgs a) {
     accA[mb] = f32x16{};
     accB[mb] = f32x16{};
   }
-  static_for<D>([&](auto set) {
-    constexpr int S = decltype(set)::value;
-    st.template load<S>(a, b, br.z, k0 + S * kPipeKeys, k1, lane);
-  });
   float dprev = 1.0f;
 
   // Step t (ring set S = t % D): tile t from set S into LDS, refill set S with
