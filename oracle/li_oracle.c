@@ -157,18 +157,20 @@ int lio_visible_count(const lio_problem* p, const lio_inputs* in, int b, int i) 
 
 /* ---- scores -------------------------------------------------------------- */
 
-/* fp64 score of key s for a row whose decoded q (n1 x d) and w (n1) are given */
+/* fp64 score of key s for a row whose decoded q (n1 x d) and w (n1) are given.
+ * krow: scratch of d doubles that receives the decoded (descaled) key row, which
+ * every head then reads. */
 static double score_row_key(const lio_problem* p, const lio_inputs* in, const double* qrow,
-                            const double* wrow, int b, int s) {
+                            const double* wrow, int b, int s, double* krow) {
   int64_t dsc;
   int64_t koff = k_offset(p, in, b, s, &dsc);
   double kd = (p->qk_dtype == LIO_E4M3) ? (double)in->k_descale[dsc] : 1.0;
+  for (int e = 0; e < p->d; ++e) krow[e] = lio_decode(p->qk_dtype, in->k, koff + e) * kd;
   double total = 0.0;
   for (int h = 0; h < p->n1; ++h) {
     double x = 0.0;
     for (int d = 0; d < p->d; ++d) {
-      double kv = lio_decode(p->qk_dtype, in->k, koff + d) * kd;
-      x += qrow[(int64_t)h * p->d + d] * kv;
+      x += qrow[(int64_t)h * p->d + d] * krow[d];
     }
     double r = x > 0.0 ? x : 0.0;                      /* ReLU */
     total += wrow[h] * r;
@@ -188,10 +190,12 @@ static void load_row(const lio_problem* p, const lio_inputs* in, int b, int i, d
 double lio_score(const lio_problem* p, const lio_inputs* in, int b, int i, int s) {
   double* qrow = (double*)malloc(sizeof(double) * (size_t)p->n1 * p->d);
   double* wrow = (double*)malloc(sizeof(double) * (size_t)p->n1);
+  double* krow = (double*)malloc(sizeof(double) * (size_t)p->d);
   load_row(p, in, b, i, qrow, wrow);
-  double v = score_row_key(p, in, qrow, wrow, b, s);
+  double v = score_row_key(p, in, qrow, wrow, b, s, krow);
   free(qrow);
   free(wrow);
+  free(krow);
   return v;
 }
 
@@ -211,7 +215,7 @@ static int cand_cmp(const void* a, const void* b) {
 }
 
 static void one_row(const lio_problem* p, const lio_inputs* in, int64_t row, int32_t* oi,
-                    float* ov, double* qrow, double* wrow) {
+                    float* ov, double* qrow, double* wrow, double* krow) {
   int b = 0, i = 0;
   int nvis = 0;
   if (lio_row_coords(p, in, row, &b, &i) == 0) nvis = lio_visible_count(p, in, b, i);
@@ -221,7 +225,7 @@ static void one_row(const lio_problem* p, const lio_inputs* in, int64_t row, int
     load_row(p, in, b, i, qrow, wrow);
     /* the visible keys are exactly 0 .. nvis-1 under both mask modes */
     for (int s = 0; s < nvis; ++s) {
-      c[s].score = score_row_key(p, in, qrow, wrow, b, s);
+      c[s].score = score_row_key(p, in, qrow, wrow, b, s, krow);
       c[s].key = s;
     }
     qsort(c, (size_t)nvis, sizeof(cand), cand_cmp);
@@ -255,12 +259,15 @@ static void* worker(void* arg) {
   const lio_problem* p = jb->p;
   double* qrow = (double*)malloc(sizeof(double) * (size_t)p->n1 * p->d);
   double* wrow = (double*)malloc(sizeof(double) * (size_t)p->n1);
+  double* krow = (double*)malloc(sizeof(double) * (size_t)p->d);
   for (int64_t j = jb->tid; j < jb->nrows; j += jb->nthreads) {
     int64_t row = jb->rows ? jb->rows[j] : j;
-    one_row(p, jb->in, row, jb->out_idx + j * p->topk, jb->out_val + j * p->topk, qrow, wrow);
+    one_row(p, jb->in, row, jb->out_idx + j * p->topk, jb->out_val + j * p->topk, qrow, wrow,
+            krow);
   }
   free(qrow);
   free(wrow);
+  free(krow);
   return NULL;
 }
 

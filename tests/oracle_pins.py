@@ -107,6 +107,30 @@ def pin_negative_weight():
     assert np.array_equal(val[0], expect[order].astype(np.float32))
 
 
+def pin_negative_zero_is_canonical():
+    # A negative weight times a positive dot product far below fp32's smallest
+    # subnormal (2^-149) is a negative fp64 score that rounds to -0 in fp32; a
+    # zero ReLU gives an exact zero.  Every written value must then be +0 (sign
+    # bit clear), while the ranking still follows the exact fp64 scores: the
+    # exact zeros first (ascending key), then the tiny negatives by magnitude.
+    g = torch.Generator().manual_seed(12)
+    S, D, d0 = 48, 128, 11
+    wt, a = -(2.0 ** -120), -40
+    q = torch.zeros(1, 1, 1, D)
+    q[..., d0] = 2.0 ** a
+    k = torch.randn(1, S, 1, D, generator=g)
+    w = torch.full((1, 1, 1), wt)
+    inst = bsnd_inst(q.bfloat16(), k.bfloat16(), w.bfloat16(), topk=S, mask_mode=0)
+    kk = inst["k"].to(torch.float64)[0, :, 0, d0].numpy()
+    expect = wt * (2.0 ** a) * np.maximum(kk, 0.0)      # exact in fp64, |x| < 2^-150
+    assert (kk > 0).any() and (kk <= 0).any()
+    idx, val = oracle.Bound(inst).forward()
+    order = np.lexsort((np.arange(S), -expect))
+    assert list(idx[0]) == list(order), "ranking by the exact fp64 scores"
+    assert (val[0] == 0).all(), "tiny scores round to zero"
+    assert not np.signbit(val[0]).any(), "-0 written where +0 is due"
+
+
 def pin_two_onehot_heads():
     g = torch.Generator().manual_seed(3)
     S, D, d0, d1 = 40, 128, 5, 90

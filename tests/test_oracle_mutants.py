@@ -24,8 +24,8 @@ MUTANTS = {
                            "return (x->key < y->key) - (x->key > y->key);"),
     "causal_off_by_one": ("long long last = (long long)i + S2 - S1;",
                           "long long last = (long long)i + S2 - S1 - 1;"),
-    "q_transposed": ("x += qrow[(int64_t)h * p->d + d] * kv;",
-                     "x += qrow[(int64_t)d * p->n1 + h] * kv;"),
+    "q_transposed": ("x += qrow[(int64_t)h * p->d + d] * krow[d];",
+                     "x += qrow[(int64_t)d * p->n1 + h] * krow[d];"),
     "pool_stride_ignored": ("return (int64_t)blk * p->k_block_stride + (int64_t)row * p->d;",
                             "return (int64_t)blk * p->block_size * p->d + (int64_t)row * p->d;"),
     "k_descale_dropped": ("double kd = (p->qk_dtype == LIO_E4M3) ? (double)in->k_descale[dsc] : 1.0;",
@@ -53,6 +53,7 @@ MUTANTS = {
     "cmp_residual_dropped": ("(long long)S2 * r + in->cmp_residual_k[b] - S1;",
                              "(long long)S2 * r - S1;"),
     "idx_offset_dropped": ("oi[j] = c[j].key + off;", "oi[j] = c[j].key;"),
+    "negative_zero_kept": ("ov[j] = (float)c[j].score + 0.0f;", "ov[j] = (float)c[j].score;"),
     "w_not_per_token": ("wrow[h] = lio_decode(p->w_dtype, in->w, t * p->n1 + h);",
                         "wrow[h] = lio_decode(p->w_dtype, in->w, h);"),
 }
