@@ -14,6 +14,11 @@ and the CPU oracle timed on a bounded sample of the same workload.
   python bench.py [--steps K] [--warmup W] [--workload prefill|decode|varlen|longfp8|tiny]
                   [--no-cpu-baseline] [--gpus 1]
 
+Without --workload the line's headline (value, roofline, cpu_baseline) is the
+prefill workload, and "workloads" holds the same record for decode (% of HBM
+bandwidth), varlen and longfp8 (% of MFMA peak), each with its own roofline and
+CPU-baseline sample, all timed in the same run.
+
 --workload gather times li_gather instead: the rows that the decode workload's
 top-2048 selects, gathered from a paged pool of 1 KiB token rows (HBM-bound).
 """
@@ -121,8 +126,33 @@ def to_device(inst, dev):
     return g
 
 
-def cpu_baseline(inst, max_rows: int, cores: int):
+def host_cpu():
+    """(model name, logical CPUs this process may run on) of the host."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return model, n
+
+
+# The host's CPU share next to one GPU: the oracle's thread pool is capped here.
+CPU_SHARE = 16
+
+
+def cpu_baseline(inst, max_rows: int):
+    """The oracle as it is, on a bounded, evenly spaced sample of the workload's rows."""
     import oracle
+    model, ncpu = host_cpu()
+    cores = min(ncpu, CPU_SHARE)
     ob = oracle.Bound(inst)
     total = ob.num_rows
     nrows = min(total, max_rows)
@@ -131,46 +161,21 @@ def cpu_baseline(inst, max_rows: int, cores: int):
     ob.forward(rows=rows, nthreads=cores)
     dt = time.perf_counter() - t0
     return {"value": len(rows) / dt, "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(rows)} of {total} query rows, evenly spaced (every "
-                      f"{total // max(1, len(rows))}th row), plain fp64 C oracle with {cores} "
-                      f"POSIX threads; {dt:.1f} s wall"}
+            "cpu_model": model, "host_cpus": ncpu,
+            "sample": f"{len(rows)} of {total} query rows, evenly spaced, plain fp64 C oracle "
+                      f"with {cores} POSIX threads (the host's CPU share next to one GPU); "
+                      f"{dt:.1f} s wall"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="prefill", choices=sorted(synth.PRESETS) + ["gather"])
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
-                    help="only run a plain copy of BYTES (counter calibration) and exit")
-    ap.add_argument("--print-kernel-hash", action="store_true")
-    args = ap.parse_args()
-    if args.print_kernel_hash:
-        print(kernel_source_hash())
-        return
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration, 4)
-        return
+# rows of the CPU-baseline sample per workload (about 5-20 s of oracle time each)
+CPU_ROWS = {"prefill": 2048, "decode": 64, "varlen": 384, "longfp8": 96, "tiny": 256}
+# the workloads timed in the default run: the headline first, then the rest of the metric
+DEFAULT_WORKLOADS = ("prefill", "decode", "varlen", "longfp8")
 
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
-              "the multi-GPU sharding is a design note, not an implemented path", file=sys.stderr)
-        sys.exit(2)
-    if not torch.cuda.is_available():
-        print("bench.py: no GPU visible", file=sys.stderr)
-        sys.exit(1)
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    binding.load()
-    if args.workload == "gather":
-        bench_gather(args, dev)
-        return
-    inst = synth.make(args.workload, args.seed)
+def run_workload(name, args, dev, steps):
+    """Times `steps` steps of li_metadata + li_forward on one workload; returns its record."""
+    inst = synth.make(name, args.seed)
     g = to_device(inst, dev)
     p = binding.problem_for(inst, g["k"])
     st, meta_bytes = binding.li_metadata_size(p)
@@ -205,7 +210,7 @@ def main():
     # holding clean lines; a fill would leave dirty ones whose write-back would
     # be charged to the next kernel.
     flush = None
-    if args.workload in HBM_BOUND:
+    if name in HBM_BOUND:
         # float32: the sum reads it in place (an integer sum would first widen
         # it to int64 in a temporary, writing 2 GiB)
         flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -225,11 +230,11 @@ def main():
             torch.cuda.synchronize()
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
         if flush is not None:
             flush.sum()
         metadata()
@@ -254,42 +259,94 @@ def main():
     pairs = visible_pairs(inst)
     flop = 2.0 * inst["n1"] * 128 * pairs
     hbm = algorithmic_bytes(inst)
-    ms_step = wall * 1000.0 / args.steps if flush is None else fwd_avg + meta_ms
-    value = rows / (ms_step / 1000.0)
-    if args.workload in HBM_BOUND:
+    # with the cache eviction inside the loop the wall clock would count it: the
+    # step is then the events' forward plus the metadata kernel
+    ms_step = wall * 1000.0 / steps if flush is None else fwd_avg + meta_ms
+    if name in HBM_BOUND:
         achieved = hbm / (fwd_avg / 1000.0) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.workload)}
+                "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(name)}
     else:
         achieved = flop / (fwd_avg / 1000.0) / 1e12
         peak = PEAK_TFLOPS[dtype]
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": measured_traffic(args.workload)}
-
-    cfg = {"workload": args.workload, "batch": inst["batch"], "seq_len_q": inst["max_seqlen_q"],
+                "frac": achieved / peak, "traffic": measured_traffic(name)}
+    cfg = {"workload": name, "batch": inst["batch"], "seq_len_q": inst["max_seqlen_q"],
            "seq_len_k": inst["max_seqlen_k"], "query_rows": rows, "heads_q": inst["n1"],
            "head_dim": 128, "topk": topk, "layout_q": inst["layout_q"],
            "layout_k": inst["layout_k"], "mask_mode": inst["mask_mode"], "seed": args.seed}
-    out = {
-        "metric": "query-tokens/s (prefill score + top-k), TFLOPS and % of MFMA peak",
-        "value": value, "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "warmup_steps_run": done, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
-        "config": cfg,
+    rec = {
+        "value": rows / (ms_step / 1000.0), "unit": "query-tokens/s", "steps": steps,
+        "warmup_steps_run": done, "ms_per_step": ms_step, "dtype": dtype, "config": cfg,
         "forward_ms": fwd_avg, "forward_ms_p10": float(np.percentile(fwd_ms, 10)),
         "forward_ms_p90": float(np.percentile(fwd_ms, 90)), "metadata_ms": meta_ms,
         "tflops": flop / (fwd_avg / 1000.0) / 1e12, "algorithmic_flop": flop,
-        "algorithmic_bytes": hbm, "visible_pairs": pairs,
-        "roofline": roof,
+        "algorithmic_bytes": hbm, "visible_pairs": pairs, "roofline": roof,
     }
-    if args.workload in HBM_BOUND:
-        out["metric"] = "query-tokens/s (paged decode score + top-k) and % of HBM bandwidth"
+    if dtype == "fp8":
+        rec["frac_of_bf16_peak"] = rec["tflops"] / PEAK_TFLOPS["bf16"]
+    del g, meta, ws, idx, val, flush
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        try:
-            cores = min(16, len(os.sched_getaffinity(0)))
-        except AttributeError:
-            cores = min(16, os.cpu_count() or 1)
-        out["cpu_baseline"] = cpu_baseline(inst, args.cpu_rows, cores)
+        rec["cpu_baseline"] = cpu_baseline(inst, CPU_ROWS.get(name, args.cpu_rows))
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, choices=sorted(synth.PRESETS) + ["gather"],
+                    help="time this workload only (default: prefill as the headline, then "
+                         "decode, varlen and longfp8 as sub-records)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (counter calibration) and exit")
+    ap.add_argument("--print-kernel-hash", action="store_true")
+    args = ap.parse_args()
+    if args.print_kernel_hash:
+        print(kernel_source_hash())
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 4)
+        return
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+              "the multi-GPU sharding is a design note, not an implemented path", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    binding.load()
+    if args.workload == "gather":
+        bench_gather(args, dev)
+        return
+    names = (args.workload,) if args.workload else DEFAULT_WORKLOADS
+    head = names[0]
+    recs = {}
+    for n in names:
+        print(f"[bench] {n}: {args.steps} steps", file=sys.stderr, flush=True)
+        recs[n] = run_workload(n, args, dev, args.steps)
+    h = recs[head]
+    out = {
+        "metric": "query-tokens/s (prefill score + top-k), TFLOPS and % of MFMA peak",
+        "value": h["value"], "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": h["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": h["dtype"], "data": "synthetic",
+    }
+    if head in HBM_BOUND:
+        out["metric"] = "query-tokens/s (paged decode score + top-k) and % of HBM bandwidth"
+    out.update({k: v for k, v in h.items() if k not in ("value", "unit", "steps", "ms_per_step",
+                                                         "dtype")})
+    if len(names) > 1:
+        out["workloads"] = {n: recs[n] for n in names[1:]}
     print(json.dumps(out), flush=True)
 
 
