@@ -249,3 +249,108 @@ def _inclusive_cumsum(v):
 def scaled_spec(name: str, **overrides) -> Spec:
     """A preset with some fields replaced (smaller parity-test variants)."""
     return dataclasses.replace(PRESETS[name], **overrides)
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the indexer backward fused with the KL loss
+# (npu_sparse_lightning_indexer_grad_kl_loss page, parameter list): the main
+# attention's q / k (+ rope parts) and its saved softmax statistics, the
+# indexer's q / k / weights, and the top-k selection sparse_indices.
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class GradSpec:
+    name: str = "grad"
+    batch: int = 1
+    s1: int = 256                  # BSND query length (= key length)
+    layout: str = "BSND"           # BSND or TND (query and key sides alike)
+    len_lo: int = 0                # TND: sequence lengths drawn in [len_lo, len_hi]
+    len_hi: int = 0
+    fixed_lengths: Optional[list] = None
+    n_main: int = 16               # main-attention query heads (one key head)
+    d_main: int = 128
+    d_rope: int = 64               # 0: no rope inputs
+    n_idx: int = 64                # index query heads
+    d_idx: int = 128
+    topk: int = 64
+    dtype: str = "bf16"            # q, k, q_rope, k_rope, qi, ki
+    w_dtype: str = "bf16"
+    w_scale: float = 1.0 / 8.0
+    scale: Optional[float] = None  # scale_value; default 1/sqrt(d_main + d_rope)
+    # saved softmax statistics per (row, head): max ~ N(max_mu, max_sd), sum ~ U[sum_lo, sum_hi]
+    max_mu: float = 3.0
+    max_sd: float = 0.5
+    sum_lo: float = 50.0
+    sum_hi: float = 500.0
+
+
+GRAD_PRESETS = {
+    "grad_tiny": GradSpec(name="grad_tiny", batch=1, s1=256, n_main=4, n_idx=8, topk=32,
+                          w_scale=1.0 / math.sqrt(8.0)),
+    # training-shaped: 64 index heads of 128, top-2048 over a 4096-token causal
+    # sequence, 32 main heads of 128 + 64 rope
+    "grad_train": GradSpec(name="grad_train", batch=1, s1=4096, n_main=32, n_idx=64,
+                           topk=2048),
+    # the same shape at a size the CPU oracle runs in full (every row, every key)
+    "grad_mid": GradSpec(name="grad_mid", batch=2, s1=1024, n_main=16, n_idx=64, topk=256),
+}
+
+
+def make_grad(spec: GradSpec | str, seed: int = 0) -> dict:
+    """One seeded backward instance (CPU tensors).  sparse_indices holds, per query
+    row, min(topk, visible) distinct keys drawn uniformly from the row's right-down
+    causal window (the shape of a top-k selection; no score is computed), in
+    random order, then -1 padding."""
+    if isinstance(spec, str):
+        spec = GRAD_PRESETS[spec]
+    g = torch.Generator().manual_seed(int(seed))
+    B = spec.batch
+    if spec.layout == "TND":
+        if spec.fixed_lengths is not None:
+            lens = [int(v) for v in spec.fixed_lengths]
+        else:
+            lens = torch.randint(spec.len_lo, spec.len_hi + 1, (B,), generator=g).tolist()
+    else:
+        lens = [spec.s1] * B
+    rows = sum(lens)
+    lead = (rows,) if spec.layout == "TND" else (B, spec.s1)
+    cast = lambda x, dt: _cast(x, dt).contiguous()
+    out = dict(name=spec.name, seed=int(seed), batch=B, layout=spec.layout, seqlens=lens,
+               max_seqlen_q=max(lens) if lens else 0, max_seqlen_k=max(lens) if lens else 0,
+               n_main=spec.n_main, d_main=spec.d_main, d_rope=spec.d_rope, n_idx=spec.n_idx,
+               d_idx=spec.d_idx, topk=spec.topk,
+               scale=spec.scale if spec.scale else 1.0 / math.sqrt(spec.d_main + spec.d_rope),
+               cu_seqlens_q=None, cu_seqlens_k=None)
+    if spec.layout == "TND":
+        cu = torch.tensor(_inclusive_cumsum(lens), dtype=torch.int32)
+        out["cu_seqlens_q"], out["cu_seqlens_k"] = cu, cu.clone()
+    out["q"] = cast(_randn(g, lead + (spec.n_main, spec.d_main)), spec.dtype)
+    out["k"] = cast(_randn(g, lead + (1, spec.d_main)), spec.dtype)
+    if spec.d_rope > 0:
+        out["q_rope"] = cast(_randn(g, lead + (spec.n_main, spec.d_rope)), spec.dtype)
+        out["k_rope"] = cast(_randn(g, lead + (1, spec.d_rope)), spec.dtype)
+    else:
+        out["q_rope"] = out["k_rope"] = None
+    out["qi"] = cast(_randn(g, lead + (spec.n_idx, spec.d_idx)), spec.dtype)
+    out["ki"] = cast(_randn(g, lead + (1, spec.d_idx)), spec.dtype)
+    out["w"] = cast(_randn(g, lead + (spec.n_idx,)) * spec.w_scale, spec.w_dtype)
+    # the selection: a seeded random subset of each row's causal window
+    sel = torch.full((rows, spec.topk), -1, dtype=torch.int32)
+    r0 = 0
+    for L in lens:
+        for i0 in range(0, L, 1024):                 # row chunks bound the draw's memory
+            i1 = min(L, i0 + 1024)
+            u = torch.rand((i1 - i0, L), generator=g)
+            lim = torch.arange(i0, i1).unsqueeze(1) + 1          # keys 0 .. i visible
+            u = torch.where(torch.arange(L).unsqueeze(0) < lim, u, torch.full_like(u, 2.0))
+            order = torch.argsort(u, dim=1)[:, :spec.topk].to(torch.int32)
+            keep = torch.arange(order.shape[1]).unsqueeze(0) < lim
+            sel[r0 + i0:r0 + i1, :order.shape[1]] = torch.where(keep, order,
+                                                                 torch.full_like(order, -1))
+        r0 += L
+    out["sparse_indices"] = sel.contiguous()
+    G = spec.n_main
+    out["softmax_max"] = (spec.max_mu + spec.max_sd * _randn(g, (rows, G))).contiguous()
+    out["softmax_sum"] = (spec.sum_lo + (spec.sum_hi - spec.sum_lo) *
+                          torch.rand((rows, G), generator=g)).contiguous()
+    return out
