@@ -17,7 +17,9 @@ and the CPU oracle timed on a bounded sample of the same workload.
 Without --workload the line's headline (value, roofline, cpu_baseline) is the
 prefill workload, and "workloads" holds the same record for decode (% of HBM
 bandwidth), varlen and longfp8 (% of MFMA peak), each with its own roofline and
-CPU-baseline sample, all timed in the same run.
+CPU-baseline sample, all timed in the same run, and for grad_train: the
+indexer backward fused with its KL loss (li_grad_kl) on a training-shaped
+problem (4096 causal tokens, 64 index heads, top-2048, 32 main heads with rope).
 
 --workload gather times li_gather instead: the rows that the decode workload's
 top-2048 selects, gathered from a paged pool of 1 KiB token rows (HBM-bound).
@@ -167,10 +169,11 @@ def cpu_baseline(inst, max_rows: int):
                       f"{dt:.1f} s wall"}
 
 
-# rows of the CPU-baseline sample per workload (about 5-20 s of oracle time each)
-CPU_ROWS = {"prefill": 2048, "decode": 64, "varlen": 384, "longfp8": 96, "tiny": 256}
+# rows of the CPU-baseline sample per workload (a few seconds to about 10 s of oracle
+# time each on 16 cores of the GPU host)
+CPU_ROWS = {"prefill": 4096, "decode": 64, "varlen": 4096, "longfp8": 320, "tiny": 256}
 # the workloads timed in the default run: the headline first, then the rest of the metric
-DEFAULT_WORKLOADS = ("prefill", "decode", "varlen", "longfp8")
+DEFAULT_WORKLOADS = ("prefill", "decode", "varlen", "longfp8", "grad_train")
 
 
 def run_workload(name, args, dev, steps):
@@ -292,12 +295,84 @@ def run_workload(name, args, dev, steps):
     return rec
 
 
+def run_grad(name, args, dev, steps):
+    """Times li_grad_kl (the backward fused with its KL loss) on a make_grad workload."""
+    inst = synth.make_grad(name, args.seed)
+    t = {n: (inst[n].to(dev) if isinstance(inst.get(n), torch.Tensor) else None)
+         for n in binding.GRAD_INPUTS}
+    p = binding.grad_problem_for(inst)
+    st, wsb = binding.li_grad_workspace_size(p)
+    assert st == 0, binding.li_status_str(st)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    run = lambda: binding.lightning_indexer_grad_kl(p, t, workspace=ws)
+    t_w = time.perf_counter()
+    done = 0
+    while done < args.warmup or time.perf_counter() - t_w < WARMUP_MIN_S:
+        run()
+        done += 1
+        if done % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        starts[k].record(stream)
+        run()
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    avg = float(np.mean(ms))
+    rows = int(sum(inst["seqlens"]))
+    pairs = int((inst["sparse_indices"] >= 0).sum())
+    # per selected (row, key) pair: index scores, d_q_index and d_k_index (2 * Ni * 128
+    # each) and the main-attention logits (2 * G * (128 + rope))
+    flop_pair = 6 * inst["n_idx"] * inst["d_idx"] + 2 * inst["n_main"] * (inst["d_main"] +
+                                                                          inst["d_rope"])
+    flop = float(flop_pair) * pairs
+    achieved = flop / (avg / 1000.0) / 1e12
+    peak = PEAK_TFLOPS["bf16" if inst["qi"].dtype == torch.bfloat16 else "fp16"]
+    rec = {
+        "value": rows / (wall / steps), "unit": "query-tokens/s", "steps": steps,
+        "warmup_steps_run": done, "ms_per_step": wall * 1000.0 / steps,
+        "dtype": "bf16" if inst["qi"].dtype == torch.bfloat16 else "fp16",
+        "config": {"workload": name, "batch": inst["batch"], "seq_len": inst["max_seqlen_q"],
+                   "query_rows": rows, "heads_main": inst["n_main"], "rope_dim": inst["d_rope"],
+                   "heads_index": inst["n_idx"], "topk": inst["topk"], "layout": inst["layout"],
+                   "seed": args.seed},
+        "forward_ms": avg, "forward_ms_p10": float(np.percentile(ms, 10)),
+        "forward_ms_p90": float(np.percentile(ms, 90)), "selected_pairs": pairs,
+        "algorithmic_flop": flop, "tflops": achieved,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": measured_traffic(name)},
+    }
+    del t, ws
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        from oracle import grad as grad_oracle
+        model, ncpu = host_cpu()
+        sample = np.linspace(0, rows - 1, 48).round().astype(np.int64)
+        t0 = time.perf_counter()
+        grad_oracle.Bound(inst).backward_rows(sample)
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {
+            "value": len(sample) / dt, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+            "cpu_model": model, "host_cpus": ncpu,
+            "sample": f"{len(sample)} of {rows} query rows, evenly spaced: loss, d_q_index and "
+                      f"d_w of each row by the plain fp64 C oracle on one thread (d_k_index "
+                      f"needs every row); {dt:.1f} s wall"}
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=None, choices=sorted(synth.PRESETS) + ["gather"],
+    ap.add_argument("--workload", default=None,
+                    choices=sorted(synth.PRESETS) + sorted(synth.GRAD_PRESETS) + ["gather"],
                     help="time this workload only (default: prefill as the headline, then "
                          "decode, varlen and longfp8 as sub-records)")
     ap.add_argument("--seed", type=int, default=0)
@@ -333,7 +408,10 @@ def main():
     recs = {}
     for n in names:
         print(f"[bench] {n}: {args.steps} steps", file=sys.stderr, flush=True)
-        recs[n] = run_workload(n, args, dev, args.steps)
+        if n in synth.GRAD_PRESETS:
+            recs[n] = run_grad(n, args, dev, args.steps)
+        else:
+            recs[n] = run_workload(n, args, dev, args.steps)
     h = recs[head]
     out = {
         "metric": "query-tokens/s (prefill score + top-k), TFLOPS and % of MFMA peak",
@@ -343,6 +421,8 @@ def main():
     }
     if head in HBM_BOUND:
         out["metric"] = "query-tokens/s (paged decode score + top-k) and % of HBM bandwidth"
+    if head in synth.GRAD_PRESETS:
+        out["metric"] = "query-tokens/s (indexer backward fused with its KL loss), % of MFMA peak"
     out.update({k: v for k, v in h.items() if k not in ("value", "unit", "steps", "ms_per_step",
                                                          "dtype")})
     if len(names) > 1:

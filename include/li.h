@@ -41,7 +41,10 @@
  *    a batch with S1_b queries and S2_b keys sees keys s <= i + S2_b - S1_b.
  *  - Exactly n = min(topk, |visible|) valid entries, stored as the prefix
  *    [0, n) of each output row; among equal scores the smaller key index wins.
- *    The order inside the prefix is ascending key index.
+ *    The order inside the prefix is not specified (the pages' consumer gathers
+ *    by index, which is order-free: aclnnSparseFlashAttentionGrad page,
+ *    calculation formula), but it is deterministic: the same inputs give
+ *    bitwise the same outputs.
  *  - No 1/sqrt(D) scale is applied.  fp8 inputs are e4m3fn codes whose real value is
  *    code * descale, with one fp32 descale per query token and per key slot.
  */
@@ -63,7 +66,9 @@ typedef enum {
   LI_ERR_UNSUPPORTED = 2,        /* valid for the pages but a shape whose working set does not
                                     fit the kernels (index or token counts past int32) */
   LI_ERR_WORKSPACE_TOO_SMALL = 3,/* metadata or workspace buffer smaller than the size query said */
-  LI_ERR_HIP = 4                 /* a HIP runtime call failed (launch error) */
+  LI_ERR_HIP = 4,                /* a HIP runtime call failed (launch error) */
+  LI_ERR_METADATA_MISMATCH = 5   /* device-side only: the metadata passed to li_forward was not
+                                    built by li_metadata for this problem (see li_forward) */
 } li_status;
 
 typedef enum {
@@ -115,7 +120,8 @@ typedef struct {
  * only: validates the scalars, makes no HIP call. */
 li_status li_metadata_size(const li_problem* p, size_t* bytes);
 
-/* Bytes of scratch device memory li_forward needs (0 is possible).  Host only. */
+/* Bytes of device workspace li_forward needs (at least 256: a status block, then the
+ * kernels' scratch).  Host only. */
 li_status li_workspace_size(const li_problem* p, size_t* bytes);
 
 /*
@@ -160,9 +166,17 @@ li_status li_metadata(const li_problem* p, const int32_t* cu_seqlens_q,
  *  output_idx_offset : NULL, or int32 [B] of offsets >= 0 added to every valid
  *                 index of batch b (the -1 padding stays); index + offset must fit
  *                 int32 (aclnnLightningIndexerV2 page, 约束说明).
- *  metadata     : filled by li_metadata for this problem.
- *  workspace    : li_workspace_size bytes of device scratch (may be NULL when that
- *                 size is 0), 256-byte aligned; its contents need no initialisation.
+ *  metadata     : filled by li_metadata for this problem.  Its header holds a
+ *                 fingerprint of the li_problem scalars it was built for; every kernel
+ *                 compares it with the fingerprint of `p` before it reads a work item.
+ *                 On a mismatch (metadata of another problem) nothing is read from the
+ *                 work list: every output slot receives -1 / -inf and the status word
+ *                 (below) becomes LI_ERR_METADATA_MISMATCH.  The call itself still
+ *                 returns LI_OK, since the check runs on the device.
+ *  workspace    : li_workspace_size bytes of device memory, 256-byte aligned; its
+ *                 contents need no initialisation.  Its first int32 is the status word:
+ *                 once the call has completed on `stream` it holds LI_OK or
+ *                 LI_ERR_METADATA_MISMATCH.
  *  sparse_indices : int32 [B, S1, 1, topk] or [T1, 1, topk].
  *  sparse_values  : fp32, same shape, or NULL to skip values (the pages'
  *                   return_value = 0).
@@ -193,7 +207,8 @@ li_status li_forward(const li_problem* p, const void* q, const void* k, const vo
  *  select_block : tokens per index (selectedBlockSize, >= 1): index i selects the
  *                 tokens i * select_block .. i * select_block + select_block - 1.
  *  block_table  : int32 [B, max_blocks_per_seq]; required iff layout_k == PA_BSND.
- *  metadata     : filled by li_metadata for p.
+ *  metadata     : filled by li_metadata for p (checked as in li_forward: with metadata
+ *                 of another problem every output row is zero bytes).
  *  out          : [rows, topk * select_block, row_bytes] bytes, 16-byte aligned.  An
  *                 index of -1, or a token at or past the sequence's key count, gives a
  *                 row of zero bytes.
@@ -203,6 +218,73 @@ li_status li_gather(const li_problem* p, const void* kv, int32_t row_bytes, int6
                     const int32_t* sparse_indices, int32_t select_block,
                     const int32_t* block_table, const void* metadata, void* out,
                     hipStream_t stream);
+
+/*
+ * Backward of the indexer fused with its KL loss (npu_sparse_lightning_indexer_grad_kl_loss
+ * page, 计算公式 items 1-4 and its parameter list).  For query token t and the keys s_j
+ * that the valid entries of sparse_indices[t] select:
+ *   I_j  = sum_h w[t,h] ReLU(S_h,j),  S_h,j = q_index[t,h,:] . k_index[s_j,:]
+ *   p_j  = sum_g exp(scale (q[t,g,:] . k[s_j,:] + q_rope[t,g,:] . k_rope[s_j,:]) - softmax_max[t,g])
+ *          / softmax_sum[t,g], normalised to sum 1 over j (the main attention's probabilities,
+ *          recomputed from the statistics its forward saved, summed over the heads)
+ *   loss = sum_t sum_j p_j (log p_j - log Softmax(I)_j)       (KL(p || Softmax(I)))
+ *   dI   = Softmax(I) - p;  d_w[t,h] = sum_j dI_j ReLU(S_h,j);  dS_h,j = dI_j w[t,h] [S_h,j > 0]
+ *   d_q_index[t,h,:] = sum_j dS_h,j k_index[s_j,:];  d_k_index[s,:] = sum over (t, j, h) with
+ *          s_j = s of dS_h,j q_index[t,h,:]
+ * Readings where the page is silent: the distributions run over the selected keys only
+ * (entries of -1, or at or past the sequence's key count, are skipped); scale_value takes
+ * the place of 1/sqrt(d); the main attention has one key head shared by its G query
+ * heads, so softmax_max / softmax_sum are [rows, G] (the page's (B, N2, S1, G) with N2 = 1);
+ * all outputs are fp32.
+ */
+typedef struct {
+  int32_t batch;                 /* B >= 0                                                  */
+  int32_t max_seqlen_q;          /* BSND: S1.  TND: an upper bound of every S1_b            */
+  int32_t max_seqlen_k;          /* BSND: S2.  TND: an upper bound of every S2_b            */
+  int32_t total_q;               /* TND: T1 (= cu_seqlens_q[B-1]); else ignored             */
+  int32_t total_k;               /* TND: T2 (= cu_seqlens_k[B-1]); else ignored             */
+  int32_t layout;                /* li_layout BSND or TND, the query and key sides alike    */
+  int32_t num_heads;             /* G: main-attention query heads, [1, 64]                  */
+  int32_t head_dim;              /* main-attention head dim: 128                            */
+  int32_t rope_dim;              /* 0 (no rope inputs) or 64                                */
+  int32_t num_heads_index;       /* indexer query heads, [1, 64]                            */
+  int32_t head_dim_index;        /* 128                                                     */
+  int32_t topk;                  /* entries per sparse_indices row, [1, 2048]               */
+  int32_t dtype;                 /* li_dtype BF16 or FP16: q, k, q_rope, k_rope, q_index,
+                                    k_index alike                                          */
+  int32_t w_dtype;               /* li_dtype BF16 or FP32                                   */
+  float scale;                   /* scale_value                                             */
+} li_grad_problem;
+
+/* Bytes of device workspace li_grad_kl needs (the per-row losses).  Host only. */
+li_status li_grad_workspace_size(const li_grad_problem* p, size_t* bytes);
+
+/*
+ * Loss and gradients of the KL objective above, enqueued on `stream` (a fill kernel for
+ * d_k_index, the row kernel, a reduction of the loss).  Device pointers owned by the
+ * caller; the library allocates nothing.
+ *  q, k         : main attention: BSND [B, S1, G, 128] / [B, S2, 1, 128], or TND [T1, G, 128] /
+ *                 [T2, 1, 128]; q_rope, k_rope the same with 64 dims (NULL iff rope_dim == 0).
+ *  q_index, k_index : [B, S1, Ni, 128] / [B, S2, 1, 128], or [T1, Ni, 128] / [T2, 1, 128].
+ *  w            : [B, S1, Ni] or [T1, Ni], w_dtype.
+ *  sparse_indices : int32 [rows, topk], sequence-local key positions (li_forward's output
+ *                 without an index offset); -1 entries are skipped.
+ *  softmax_max, softmax_sum : fp32 [rows, G].
+ *  cu_seqlens_q, cu_seqlens_k : int32 [B] inclusive prefix sums; required iff TND.
+ *  workspace    : li_grad_workspace_size bytes, 16-byte aligned.
+ *  d_q_index    : fp32 [rows, Ni, 128];  d_w : fp32 [rows, Ni];  d_k_index : fp32 [keys, 128]
+ *                 (fully overwritten; d_k_index is summed with fp32 atomics, so its low bits
+ *                 may differ from run to run);  loss : fp32 [1], the sum over the rows (the
+ *                 per-row losses stay in the workspace as fp32 [rows]).
+ * Tensors of 16-bit elements and w must be 16-byte aligned.
+ */
+li_status li_grad_kl(const li_grad_problem* p, const void* q, const void* k, const void* q_rope,
+                     const void* k_rope, const void* q_index, const void* k_index, const void* w,
+                     const int32_t* sparse_indices, const float* softmax_max,
+                     const float* softmax_sum, const int32_t* cu_seqlens_q,
+                     const int32_t* cu_seqlens_k, void* workspace, size_t workspace_bytes,
+                     float* d_q_index, float* d_k_index, float* d_w, float* loss,
+                     hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* li_status_str(li_status s);

@@ -61,6 +61,8 @@ def _load(path):
     vp = ctypes.c_void_p
     L.liog_backward.argtypes = [P, I, vp, vp, vp, vp, ctypes.c_int]
     L.liog_backward.restype = ctypes.c_int
+    L.liog_backward_rows.argtypes = [P, I, vp, ctypes.c_int64, vp, vp, vp]
+    L.liog_backward_rows.restype = ctypes.c_int
     L.liog_num_rows.argtypes = [P, I]
     L.liog_num_rows.restype = ctypes.c_int64
     L.liog_num_keys.argtypes = [P, I]
@@ -143,3 +145,16 @@ class Bound:
         if rc != 0:
             raise ValueError("gradient oracle rejected the problem")
         return loss, dqi, dki, dw
+
+    def backward_rows(self, rows):
+        """(loss [n], d_qi [n, Ni, Di], d_w [n, Ni]) of the listed rows (no d_ki)."""
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        Ni, Di = self.inst["n_idx"], self.inst["d_idx"]
+        loss = np.empty(len(rows))
+        dqi = np.empty((len(rows), Ni, Di))
+        dw = np.empty((len(rows), Ni))
+        rc = lib().liog_backward_rows(ctypes.byref(self.p), ctypes.byref(self.i), rows.ctypes.data,
+                                      len(rows), loss.ctypes.data, dqi.ctypes.data, dw.ctypes.data)
+        if rc != 0:
+            raise ValueError("gradient oracle rejected the rows")
+        return loss, dqi, dw

@@ -287,3 +287,28 @@ int liog_backward(const liog_problem* p, const liog_inputs* in, double* loss_row
   if (!loss_rows) free(lr);
   return rc;
 }
+
+int liog_backward_rows(const liog_problem* p, const liog_inputs* in, const int64_t* rows,
+                       int64_t nrows, double* loss, double* d_qi, double* d_w) {
+  if (!p || !in || !rows || !loss || !d_qi || !d_w) return -1;
+  const int64_t total = liog_num_rows(p, in);
+  const int K = p->topk, Ni = p->n_idx, Di = p->d_idx;
+  double* l1 = (double*)malloc(sizeof(double) * (size_t)(total ? total : 1));
+  double* q1 = (double*)malloc(sizeof(double) * (size_t)(total ? total : 1) * Ni * Di);
+  double* w1 = (double*)malloc(sizeof(double) * (size_t)(total ? total : 1) * Ni);
+  double* dI = (double*)malloc(sizeof(double) * (size_t)K);
+  int rc = 0;
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t t = rows[r];
+    if (t < 0 || t >= total) { rc = -1; break; }
+    one_row(p, in, t, l1, q1, w1, dI);
+    loss[r] = l1[t];
+    memcpy(d_qi + r * Ni * Di, q1 + t * Ni * Di, sizeof(double) * (size_t)Ni * Di);
+    memcpy(d_w + r * Ni, w1 + t * Ni, sizeof(double) * (size_t)Ni);
+  }
+  free(l1);
+  free(q1);
+  free(w1);
+  free(dI);
+  return rc;
+}

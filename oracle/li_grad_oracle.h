@@ -78,10 +78,16 @@ int64_t liog_num_keys(const liog_problem* p, const liog_inputs* in);
 /* The loss of every row (loss_rows [rows]) and the gradients: d_qi [rows, Ni, Di],
  * d_ki [keys, Di], d_w [rows, Ni], all fp64 and fully overwritten.  Any output
  * pointer may be NULL to skip it.  Rows are shared by `nthreads` POSIX threads;
- * d_ki is accumulated afterwards in row order by one thread.  Returns 0, or -1 on
- * an invalid argument. */
+ * d_ki is accumulated afterwards, each key's sum over the rows in row order (the
+ * threads split the keys), so no bit depends on the thread count.  Returns 0, or
+ * -1 on an invalid argument. */
 int liog_backward(const liog_problem* p, const liog_inputs* in, double* loss_rows,
                   double* d_qi, double* d_ki, double* d_w, int nthreads);
+
+/* The same outputs for the listed rows only (no d_ki): loss [nrows], d_qi [nrows, Ni, Di],
+ * d_w [nrows, Ni].  One thread.  Returns 0, or -1 on an invalid argument. */
+int liog_backward_rows(const liog_problem* p, const liog_inputs* in, const int64_t* rows,
+                       int64_t nrows, double* loss, double* d_qi, double* d_w);
 
 /* Exact value of one element code (pins). */
 double liog_decode(int dtype, const void* ptr, int64_t index);

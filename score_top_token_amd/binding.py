@@ -25,10 +25,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblightnin
 LAYOUT = {"BSND": 0, "TND": 1, "PA_BSND": 2, "PA_BBND": 2}
 DTYPE = {torch.bfloat16: 0, torch.float8_e4m3fn: 1, torch.float32: 2, torch.float16: 3}
 STATUS = {0: "LI_OK", 1: "LI_ERR_INVALID_ARGUMENT", 2: "LI_ERR_UNSUPPORTED",
-          3: "LI_ERR_WORKSPACE_TOO_SMALL", 4: "LI_ERR_HIP"}
+          3: "LI_ERR_WORKSPACE_TOO_SMALL", 4: "LI_ERR_HIP", 5: "LI_ERR_METADATA_MISMATCH"}
 
 EXPORTED = ("li_metadata_size", "li_workspace_size", "li_metadata", "li_forward", "li_gather",
-            "li_status_str")
+            "li_grad_workspace_size", "li_grad_kl", "li_status_str")
 
 
 class Problem(ctypes.Structure):
@@ -44,6 +44,20 @@ class Problem(ctypes.Structure):
         ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
         ("max_blocks_per_seq", ctypes.c_int32), ("cmp_ratio", ctypes.c_int32),
         ("k_block_stride", ctypes.c_int64),
+    ]
+
+
+class GradProblem(ctypes.Structure):
+    """Mirror of li_grad_problem."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("max_seqlen_q", ctypes.c_int32),
+        ("max_seqlen_k", ctypes.c_int32), ("total_q", ctypes.c_int32),
+        ("total_k", ctypes.c_int32), ("layout", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("rope_dim", ctypes.c_int32),
+        ("num_heads_index", ctypes.c_int32), ("head_dim_index", ctypes.c_int32),
+        ("topk", ctypes.c_int32), ("dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
     ]
 
 
@@ -72,10 +86,13 @@ def load():
                                  vp, vp]
         L.li_gather.argtypes = [P, vp, ctypes.c_int32, ctypes.c_int64, vp, ctypes.c_int32, vp, vp,
                                 vp, vp]
+        GP = ctypes.POINTER(GradProblem)
+        L.li_grad_workspace_size.argtypes = [GP, ctypes.POINTER(sz)]
+        L.li_grad_kl.argtypes = [GP] + [vp] * 12 + [vp, sz, vp, vp, vp, vp, vp]
         L.li_status_str.argtypes = [ctypes.c_int]
         L.li_status_str.restype = ctypes.c_char_p
         for n in ("li_metadata_size", "li_workspace_size", "li_metadata", "li_forward",
-                  "li_gather"):
+                  "li_gather", "li_grad_workspace_size", "li_grad_kl"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -116,6 +133,20 @@ def li_gather(p: Problem, kv, row_bytes, kv_block_stride, sparse_indices, select
               block_table, metadata, out, stream) -> int:
     return load().li_gather(ctypes.byref(p), kv, row_bytes, kv_block_stride, sparse_indices,
                             select_block, block_table, metadata, out, stream)
+
+
+def li_grad_workspace_size(p: GradProblem) -> tuple[int, int]:
+    n = ctypes.c_size_t(0)
+    st = load().li_grad_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    return st, n.value
+
+
+def li_grad_kl(p: GradProblem, q, k, q_rope, k_rope, q_index, k_index, w, sparse_indices,
+               softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_k, workspace, workspace_bytes,
+               d_q_index, d_k_index, d_w, loss, stream) -> int:
+    return load().li_grad_kl(ctypes.byref(p), q, k, q_rope, k_rope, q_index, k_index, w,
+                             sparse_indices, softmax_max, softmax_sum, cu_seqlens_q, cu_seqlens_k,
+                             workspace, workspace_bytes, d_q_index, d_k_index, d_w, loss, stream)
 
 
 def li_status_str(status: int) -> str:
@@ -194,7 +225,9 @@ def lightning_indexer(p: Problem, q, k, w, *, metadata: torch.Tensor, q_descale=
                       k_descale=None, cu_seqlens_q=None, cu_seqlens_k=None, seqused_k=None,
                       cmp_residual_k=None, block_table=None, output_idx_offset=None,
                       return_value: int = 1, workspace=None, out=None):
-    """Runs li_forward; returns (sparse_indices, sparse_values or None)."""
+    """Runs li_forward; returns (sparse_indices, sparse_values or None).  Pass a
+    `workspace` (uint8, li_workspace_size bytes) to read its status word with
+    forward_status afterwards."""
     st, ws_bytes = li_workspace_size(p)
     _check(st, "li_workspace_size")
     dev = q.device
@@ -217,6 +250,12 @@ def lightning_indexer(p: Problem, q, k, w, *, metadata: torch.Tensor, q_descale=
                       metadata.data_ptr(), _ptr(workspace), wsb, idx.data_ptr(), _ptr(val),
                       stream), "li_forward")
     return idx, val
+
+
+def forward_status(workspace: torch.Tensor) -> int:
+    """The status word li_forward left at the start of its workspace (0 = LI_OK,
+    5 = LI_ERR_METADATA_MISMATCH); waits for the work queued on the device."""
+    return int(workspace[:4].view(torch.int32).item())
 
 
 def gather_selected(p: Problem, kv: torch.Tensor, sparse_indices: torch.Tensor, *,
@@ -269,3 +308,50 @@ def problem_for(inst: dict, k_dev: Optional[torch.Tensor] = None) -> Problem:
                         batch_size=inst["batch"], max_seqlen_q=inst["max_seqlen_q"],
                         max_seqlen_k=inst["max_seqlen_k"], block_table=inst.get("block_table"),
                         cmp_ratio=inst.get("cmp_ratio", 1) or 1)
+
+
+# ---------------------------------------------------------------------------
+# backward of the indexer fused with its KL loss
+# ---------------------------------------------------------------------------
+
+def grad_problem_for(inst: dict) -> GradProblem:
+    """GradProblem scalars of a synth.make_grad instance."""
+    p = GradProblem()
+    p.batch = inst["batch"]
+    p.max_seqlen_q = inst["max_seqlen_q"]
+    p.max_seqlen_k = inst["max_seqlen_k"]
+    p.layout = LAYOUT[inst["layout"]]
+    if inst["layout"] == "TND":
+        p.total_q = p.total_k = int(sum(inst["seqlens"]))
+    p.num_heads, p.head_dim, p.rope_dim = inst["n_main"], inst["d_main"], inst["d_rope"]
+    p.num_heads_index, p.head_dim_index = inst["n_idx"], inst["d_idx"]
+    p.topk = inst["topk"]
+    p.dtype = DTYPE.get(inst["qi"].dtype, -1)
+    p.w_dtype = DTYPE.get(inst["w"].dtype, -1)
+    p.scale = float(inst["scale"])
+    return p
+
+
+GRAD_INPUTS = ("q", "k", "q_rope", "k_rope", "qi", "ki", "w", "sparse_indices", "softmax_max",
+               "softmax_sum", "cu_seqlens_q", "cu_seqlens_k")
+
+
+def lightning_indexer_grad_kl(p: GradProblem, t: dict, workspace=None):
+    """Runs li_grad_kl on device tensors (a dict with the GRAD_INPUTS names);
+    returns (loss [1], d_q_index, d_k_index, d_w), fp32 on the device."""
+    dev = t["qi"].device
+    rows = t["qi"].shape[0] * (t["qi"].shape[1] if t["qi"].dim() == 4 else 1)
+    keys = t["ki"].numel() // t["ki"].shape[-1]
+    st, wsb = li_grad_workspace_size(p)
+    _check(st, "li_grad_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    dq = torch.empty(t["qi"].shape, dtype=torch.float32, device=dev)
+    dk = torch.empty((keys, p.head_dim_index), dtype=torch.float32, device=dev)
+    dw = torch.empty((rows, p.num_heads_index), dtype=torch.float32, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(li_grad_kl(p, *[_ptr(t.get(n)) for n in GRAD_INPUTS], workspace.data_ptr(),
+                      workspace.numel(), dq.data_ptr(), dk.data_ptr(), dw.data_ptr(),
+                      loss.data_ptr(), stream), "li_grad_kl")
+    return loss, dq, dk, dw

@@ -16,7 +16,8 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblightning_indexer.so")
-SOURCES = ["li_host.cpp", "li_metadata.hip", "li_prefill.hip", "li_decode.hip", "li_gather.hip"]
+SOURCES = ["li_host.cpp", "li_metadata.hip", "li_prefill.hip", "li_decode.hip", "li_gather.hip",
+           "li_grad.hip"]
 ARCH = os.environ.get("LI_OFFLOAD_ARCH", "gfx950")
 
 
@@ -27,12 +28,18 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _flags():
-    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-x", "hip",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            # MFMA results straight into VGPRs, where the epilogue reads them
-            "-mllvm", "-amdgpu-mfma-vgpr-form",
-            "-Wall", "-Wno-unused-function", "-I", os.path.join(HERE, "..", "include")]
+# The backward kernel keeps more accumulators than fit the VGPRs: its MFMA
+# results stay free to live in the accumulation registers.
+AGPR_SOURCES = {"li_grad.hip"}
+
+
+def _flags(src=""):
+    f = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-x", "hip",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    if src not in AGPR_SOURCES:
+        # MFMA results straight into VGPRs, where the epilogue reads them
+        f += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    return f + ["-Wall", "-Wno-unused-function", "-I", os.path.join(HERE, "..", "include")]
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
@@ -43,7 +50,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
         def compile_one(src):
             obj = os.path.join(tmpdir, src + ".o")
-            cmd = [hipcc, *_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc, *_flags(src), "-c", os.path.join(CSRC, src), "-o", obj]
             res = subprocess.run(cmd, capture_output=True, text=True)
             out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                             if "packed-fp32-ops" not in l)

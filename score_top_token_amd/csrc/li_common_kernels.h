@@ -28,6 +28,33 @@ __device__ inline int row_limit(const KArgs& a, int b, int i, int s1, int s2) {
   return n >= s2 ? s2 : (int)n;
 }
 
+// The metadata header holds the fingerprint of the problem li_metadata built it
+// for (lightning_indexer page, Prototype: the metadata call serves the indexer
+// call of the same problem).  A kernel compares it with its own before reading
+// any item.
+__device__ inline bool meta_matches(const KArgs& a) {
+  const MetaHeader* h = reinterpret_cast<const MetaHeader*>(a.meta);
+  return h->magic == kMetaMagic && h->fingerprint == a.fingerprint;
+}
+
+// Records the call's status in the workspace (workgroup 0) and, when the
+// metadata belongs to another problem, writes -1 / -inf into every output slot
+// (the grid shares the rows, whose count comes from the problem, not from the
+// metadata).  Returns whether the metadata matches; the caller then returns.
+__device__ inline bool check_meta(const KArgs& a) {
+  const bool ok = meta_matches(a);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && a.status) a.status[0] = ok ? 0 : kStatusMetaMismatch;
+  if (!ok) {
+    const int64_t n = (int64_t)a.rows * a.topk;
+    const int64_t step = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += step) {
+      a.out_idx[e] = -1;
+      if (a.out_val) a.out_val[e] = -__builtin_inff();
+    }
+  }
+  return ok;
+}
+
 // Offset added to the written indices of batch b (output_idx_offset), else 0.
 __device__ inline int index_offset(const KArgs& a, int b) { return a.idx_off ? a.idx_off[b] : 0; }
 

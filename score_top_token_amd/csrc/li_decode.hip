@@ -40,6 +40,7 @@ void split_kernel(KArgs a) {
   constexpr int D = kDecodeDepth;
   constexpr int TILE = kPipeKeys * M::RB;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  if (!check_meta(a)) return;
   const MetaHeader* hdr = reinterpret_cast<const MetaHeader*>(a.meta);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int it = blockIdx.x * kDecodeWaves + wave;
@@ -526,6 +527,7 @@ __device__ __forceinline__ void select_row(SelShared& sh, const Row& row, int to
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(KArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   SelShared& sh = *reinterpret_cast<SelShared*>(smem);
+  if (!check_meta(a)) return;
   const int r = blockIdx.x;
   const int b = r / a.s1max, i = r - (r / a.s1max) * a.s1max;
   if (b >= a.batch) return;

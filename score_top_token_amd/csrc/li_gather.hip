@@ -35,6 +35,13 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(KArgs a, GatherA
   const int r = blockIdx.x / slices;
   const int j0 = (blockIdx.x - r * slices) * kGatherRows;
   const int nj = min(kGatherRows, per_row - j0);
+  if (!meta_matches(a)) {
+    // metadata of another problem: this workgroup's rows come out as zeros
+    unsigned char* o = g.out + ((int64_t)r * per_row + j0) * g.row_bytes;
+    for (int e = threadIdx.x; e < nj * (g.row_bytes >> 4); e += kGatherThreads)
+      reinterpret_cast<i32x4*>(o)[e] = i32x4{0, 0, 0, 0};
+    return;
+  }
   const int b = row_batch(a, r);
   const int4 br = batch_rec(a, b);                         // q_off, s1, k_off, s2
   const int chunks = g.row_bytes >> 4;                     // 16-byte chunks per row

@@ -148,6 +148,8 @@ li_status make_plan(const li_problem* p, Plan* pl) {
     pl->cap = cap;
     pl->lds_prefill = fixed + (size_t)waves * cap * 8;
   }
+  // the status block ahead of the kernels' scratch
+  pl->ws_bytes += kStatusBytes;
   if (items > INT32_MAX / 16) return LI_ERR_UNSUPPORTED;
   pl->max_items = (int32_t)items;
   pl->off_batch = sizeof(MetaHeader);
@@ -160,6 +162,25 @@ li_status make_plan(const li_problem* p, Plan* pl) {
 }
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+// FNV-1a over every scalar of the problem: li_metadata stores it in the
+// metadata header, and each kernel of li_forward / li_gather compares it with
+// the fingerprint of its own problem before it reads an item.
+uint32_t fingerprint(const li_problem* p) {
+  uint32_t h = 2166136261u;
+  auto mix = [&](int64_t v) {
+    for (int i = 0; i < 8; ++i) {
+      h ^= (uint32_t)((uint64_t)v >> (8 * i)) & 0xFFu;
+      h *= 16777619u;
+    }
+  };
+  const int64_t f[] = {p->batch, p->max_seqlen_q, p->max_seqlen_k, p->total_q, p->total_k,
+                       p->num_heads_q, p->num_heads_k, p->head_dim, p->topk, p->layout_q,
+                       p->layout_k, p->mask_mode, p->qk_dtype, p->w_dtype, p->block_size,
+                       p->num_blocks, p->max_blocks_per_seq, p->cmp_ratio, p->k_block_stride};
+  for (int64_t v : f) mix(v);
+  return h;
+}
 
 // Pointer presence rules shared by li_metadata and li_forward
 // (aclnnLightningIndexerV2 page, 约束说明: cu_seqlens only with TND layouts,
@@ -206,6 +227,8 @@ KArgs base_args(const li_problem* p, const Plan& pl, void* metadata) {
   a.off_counts = (int32_t)pl.off_counts;
   a.off_starts = (int32_t)pl.off_starts;
   a.off_items = (int32_t)pl.off_items;
+  a.fingerprint = fingerprint(p);
+  a.rows = (int32_t)query_rows(p);
   return a;
 }
 
@@ -250,15 +273,18 @@ li_status li_metadata(const li_problem* p, const int32_t* cu_seqlens_q, const in
   return launch_metadata(a, pl.mode, stream) == hipSuccess ? LI_OK : LI_ERR_HIP;
 }
 
-li_status li_forward(const li_problem* p, const void* q, const void* k, const void* w,
-                     const float* q_descale, const float* k_descale, const int32_t* cu_seqlens_q,
-                     const int32_t* cu_seqlens_k, const int32_t* seqused_k,
-                     const int32_t* cmp_residual_k, const int32_t* block_table,
-                     const int32_t* output_idx_offset, const void* metadata, void* workspace,
-                     size_t workspace_bytes, int32_t* sparse_indices, float* sparse_values,
-                     hipStream_t stream) {
-  Plan pl;
-  li_status st = make_plan(p, &pl);
+}  // extern "C"
+
+namespace {
+
+// Every check of li_forward that needs neither the workspace nor device data.
+li_status forward_checks(const li_problem* p, Plan* pl, const void* q, const void* k,
+                         const void* w, const float* q_descale, const float* k_descale,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                         const int32_t* seqused_k, const int32_t* cmp_residual_k,
+                         const int32_t* block_table, const void* metadata,
+                         const int32_t* sparse_indices) {
+  li_status st = make_plan(p, pl);
   if (st != LI_OK) return st;
   st = validate_lengths(p, cu_seqlens_q, cu_seqlens_k, seqused_k, cmp_residual_k);
   if (st != LI_OK) return st;
@@ -269,10 +295,18 @@ li_status li_forward(const li_problem* p, const void* q, const void* k, const vo
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 16) || !aligned(metadata, 16))
     return LI_ERR_INVALID_ARGUMENT;
   if (fp8 && (!aligned(q_descale, 4) || !aligned(k_descale, 4))) return LI_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < pl.ws_bytes) return LI_ERR_WORKSPACE_TOO_SMALL;
-  if (pl.ws_bytes > 0 && (!workspace || !aligned(workspace, 16))) return LI_ERR_INVALID_ARGUMENT;
-  if (query_rows(p) == 0) return LI_OK;
+  return LI_OK;
+}
 
+// The launches of li_forward once every argument has been checked; `workspace`
+// holds pl.ws_bytes (status block first).
+li_status forward_launch(const li_problem* p, const Plan& pl, const void* q, const void* k,
+                         const void* w, const float* q_descale, const float* k_descale,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                         const int32_t* seqused_k, const int32_t* cmp_residual_k,
+                         const int32_t* block_table, const int32_t* output_idx_offset,
+                         const void* metadata, void* workspace, int32_t* sparse_indices,
+                         float* sparse_values, hipStream_t stream) {
   KArgs a = base_args(p, pl, const_cast<void*>(metadata));
   a.q = q;
   a.k = k;
@@ -285,7 +319,8 @@ li_status li_forward(const li_problem* p, const void* q, const void* k, const vo
   a.seqused_k = seqused_k;
   a.cmp_res = cmp_residual_k;
   a.idx_off = output_idx_offset;
-  a.ws = static_cast<float*>(workspace);
+  a.status = static_cast<int32_t*>(workspace);
+  a.ws = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + kStatusBytes);
   if (pl.mode == kModeDecode)
     a.seg_mm = a.ws + (size_t)p->batch * p->max_seqlen_q * pl.ws_row_stride;
   a.out_idx = sparse_indices;
@@ -305,6 +340,29 @@ li_status li_forward(const li_problem* p, const void* q, const void* k, const vo
       e = launch_select(a, p->batch * p->max_seqlen_q, pl.lds_select, stream);
   }
   return e == hipSuccess ? LI_OK : LI_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+li_status li_forward(const li_problem* p, const void* q, const void* k, const void* w,
+                     const float* q_descale, const float* k_descale, const int32_t* cu_seqlens_q,
+                     const int32_t* cu_seqlens_k, const int32_t* seqused_k,
+                     const int32_t* cmp_residual_k, const int32_t* block_table,
+                     const int32_t* output_idx_offset, const void* metadata, void* workspace,
+                     size_t workspace_bytes, int32_t* sparse_indices, float* sparse_values,
+                     hipStream_t stream) {
+  Plan pl;
+  li_status st = forward_checks(p, &pl, q, k, w, q_descale, k_descale, cu_seqlens_q, cu_seqlens_k,
+                                seqused_k, cmp_residual_k, block_table, metadata, sparse_indices);
+  if (st != LI_OK) return st;
+  if (workspace_bytes < pl.ws_bytes) return LI_ERR_WORKSPACE_TOO_SMALL;
+  if (pl.ws_bytes > 0 && (!workspace || !aligned(workspace, 16))) return LI_ERR_INVALID_ARGUMENT;
+  if (query_rows(p) == 0) return LI_OK;
+  return forward_launch(p, pl, q, k, w, q_descale, k_descale, cu_seqlens_q, cu_seqlens_k,
+                        seqused_k, cmp_residual_k, block_table, output_idx_offset, metadata,
+                        workspace, sparse_indices, sparse_values, stream);
 }
 
 li_status li_gather(const li_problem* p, const void* kv, int32_t row_bytes, int64_t kv_block_stride,
@@ -337,6 +395,105 @@ li_status li_gather(const li_problem* p, const void* kv, int32_t row_bytes, int6
   return launch_gather(a, g, rows, stream) == hipSuccess ? LI_OK : LI_ERR_HIP;
 }
 
+// ---- backward fused with the KL loss -------------------------------------------
+
+static li_status grad_validate(const li_grad_problem* p) {
+  if (!p) return LI_ERR_INVALID_ARGUMENT;
+  if (p->batch < 0 || p->max_seqlen_q < 0 || p->max_seqlen_k < 0) return LI_ERR_INVALID_ARGUMENT;
+  if (p->layout != LI_LAYOUT_BSND && p->layout != LI_LAYOUT_TND) return LI_ERR_INVALID_ARGUMENT;
+  if (p->layout == LI_LAYOUT_TND && (p->total_q < 0 || p->total_k < 0))
+    return LI_ERR_INVALID_ARGUMENT;
+  if (p->num_heads < 1 || p->num_heads > kMaxHeads) return LI_ERR_INVALID_ARGUMENT;
+  if (p->num_heads_index < 1 || p->num_heads_index > kMaxHeads) return LI_ERR_INVALID_ARGUMENT;
+  if (p->head_dim != kHeadDim || p->head_dim_index != kHeadDim) return LI_ERR_INVALID_ARGUMENT;
+  if (p->rope_dim != 0 && p->rope_dim != 64) return LI_ERR_INVALID_ARGUMENT;
+  if (p->topk < 1 || p->topk > kMaxTopk) return LI_ERR_INVALID_ARGUMENT;
+  if (p->dtype != LI_DT_BF16 && p->dtype != LI_DT_FP16) return LI_ERR_INVALID_ARGUMENT;
+  if (p->w_dtype != LI_DT_BF16 && p->w_dtype != LI_DT_FP32) return LI_ERR_INVALID_ARGUMENT;
+  if (!(p->scale == p->scale)) return LI_ERR_INVALID_ARGUMENT;
+  const int64_t rows = p->layout == LI_LAYOUT_TND ? p->total_q : (int64_t)p->batch * p->max_seqlen_q;
+  const int64_t keys = p->layout == LI_LAYOUT_TND ? p->total_k : (int64_t)p->batch * p->max_seqlen_k;
+  if (rows > INT32_MAX / 2 || keys * kHeadDim > INT32_MAX * (int64_t)64) return LI_ERR_UNSUPPORTED;
+  return LI_OK;
+}
+
+static int64_t grad_rows(const li_grad_problem* p) {
+  return p->layout == LI_LAYOUT_TND ? p->total_q : (int64_t)p->batch * p->max_seqlen_q;
+}
+
+static int64_t grad_keys(const li_grad_problem* p) {
+  return p->layout == LI_LAYOUT_TND ? p->total_k : (int64_t)p->batch * p->max_seqlen_k;
+}
+
+li_status li_grad_workspace_size(const li_grad_problem* p, size_t* bytes) {
+  if (!bytes) return LI_ERR_INVALID_ARGUMENT;
+  li_status st = grad_validate(p);
+  if (st != LI_OK) return st;
+  *bytes = align_up((size_t)grad_rows(p) * 4, 256) + 256;
+  return LI_OK;
+}
+
+li_status li_grad_kl(const li_grad_problem* p, const void* q, const void* k, const void* q_rope,
+                     const void* k_rope, const void* q_index, const void* k_index, const void* w,
+                     const int32_t* sparse_indices, const float* softmax_max,
+                     const float* softmax_sum, const int32_t* cu_seqlens_q,
+                     const int32_t* cu_seqlens_k, void* workspace, size_t workspace_bytes,
+                     float* d_q_index, float* d_k_index, float* d_w, float* loss,
+                     hipStream_t stream) {
+  li_status st = grad_validate(p);
+  if (st != LI_OK) return st;
+  size_t need = 0;
+  li_grad_workspace_size(p, &need);
+  const bool tnd = p->layout == LI_LAYOUT_TND;
+  if (tnd != (cu_seqlens_q != nullptr) || tnd != (cu_seqlens_k != nullptr))
+    return LI_ERR_INVALID_ARGUMENT;
+  if ((p->rope_dim > 0) != (q_rope != nullptr) || (p->rope_dim > 0) != (k_rope != nullptr))
+    return LI_ERR_INVALID_ARGUMENT;
+  if (!q || !k || !q_index || !k_index || !w || !sparse_indices || !softmax_max || !softmax_sum ||
+      !workspace || !d_q_index || !d_k_index || !d_w || !loss)
+    return LI_ERR_INVALID_ARGUMENT;
+  for (const void* ptr : {q, k, q_index, k_index, w})
+    if (!aligned(ptr, 16)) return LI_ERR_INVALID_ARGUMENT;
+  if (p->rope_dim > 0 && (!aligned(q_rope, 16) || !aligned(k_rope, 16))) return LI_ERR_INVALID_ARGUMENT;
+  if (!aligned(workspace, 16) || !aligned(sparse_indices, 4) || !aligned(softmax_max, 4) ||
+      !aligned(softmax_sum, 4) || !aligned(d_q_index, 4) || !aligned(d_k_index, 4) ||
+      !aligned(d_w, 4) || !aligned(loss, 4))
+    return LI_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < need) return LI_ERR_WORKSPACE_TOO_SMALL;
+  GradArgs g;
+  memset(&g, 0, sizeof(g));
+  g.q = q;
+  g.k = k;
+  g.q_rope = q_rope;
+  g.k_rope = k_rope;
+  g.qi = q_index;
+  g.ki = k_index;
+  g.w = w;
+  g.sel = sparse_indices;
+  g.smax = softmax_max;
+  g.ssum = softmax_sum;
+  g.cu_q = cu_seqlens_q;
+  g.cu_k = cu_seqlens_k;
+  g.d_qi = d_q_index;
+  g.d_ki = d_k_index;
+  g.d_w = d_w;
+  g.loss = loss;
+  g.loss_rows = static_cast<float*>(workspace);
+  g.keys = grad_keys(p);
+  g.rows = (int32_t)grad_rows(p);
+  g.batch = p->batch;
+  g.s1 = p->max_seqlen_q;
+  g.s2 = p->max_seqlen_k;
+  g.layout = p->layout;
+  g.G = p->num_heads;
+  g.Ni = p->num_heads_index;
+  g.topk = p->topk;
+  g.topk_pad = (int32_t)align_up(p->topk, 32);
+  g.scale = p->scale;
+  return launch_grad(g, p->dtype, p->w_dtype, p->rope_dim > 0, stream) == hipSuccess ? LI_OK
+                                                                                     : LI_ERR_HIP;
+}
+
 const char* li_status_str(li_status s) {
   switch (s) {
     case LI_OK: return "LI_OK";
@@ -344,6 +501,7 @@ const char* li_status_str(li_status s) {
     case LI_ERR_UNSUPPORTED: return "LI_ERR_UNSUPPORTED";
     case LI_ERR_WORKSPACE_TOO_SMALL: return "LI_ERR_WORKSPACE_TOO_SMALL";
     case LI_ERR_HIP: return "LI_ERR_HIP";
+    case LI_ERR_METADATA_MISMATCH: return "LI_ERR_METADATA_MISMATCH";
     default: return "LI_UNKNOWN_STATUS";
   }
 }

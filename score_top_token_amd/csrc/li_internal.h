@@ -32,6 +32,11 @@ constexpr int kWideScratch = 2048 * 4 + 2 * 64 * 4 + 256 * 4;
 constexpr int kDenseSlots = 512;         // resident dense workgroups: 2 per CU on 256 CUs
 constexpr size_t kDenseGlobalMaxBytes = size_t(1) << 31;   // workspace cap of that mode
 constexpr int kMetaMagic = 0x4C494D44;  // "LIMD"
+// The workspace starts with a status block: int32 word 0 receives the call's
+// status (0, or kStatusMetaMismatch when the metadata was built for another
+// problem); the kernels' scratch follows it.
+constexpr size_t kStatusBytes = 256;
+constexpr int32_t kStatusMetaMismatch = 5;   // = LI_ERR_METADATA_MISMATCH
 
 enum Mode : int32_t { kModeDense = 0, kModeStream = 1, kModeDecode = 2, kModeDenseGlobal = 3 };
 
@@ -50,7 +55,8 @@ struct MetaHeader {
   int32_t magic;
   int32_t batch;
   int32_t max_items;
-  int32_t pad[58];
+  uint32_t fingerprint;   // of the li_problem the metadata was built for
+  int32_t pad[57];
 };
 static_assert(sizeof(MetaHeader) == 256, "metadata header is 256 bytes");
 
@@ -90,6 +96,7 @@ struct KArgs {
   float* seg_mm;            // decode: (min, max) score of each segment, seg_mm_stride pairs per row
   int32_t* out_idx;
   float* out_val;
+  int32_t* status;          // workspace status word, or NULL (li_gather)
   int64_t k_block_stride_bytes;   // bytes between paged blocks
   int64_t ws_row_stride;
   int32_t seg_mm_stride;
@@ -99,6 +106,8 @@ struct KArgs {
   int32_t block_size, block_shift, max_blocks_per_seq;
   int32_t cap, dcap, chunk, max_items, rows_per_item;
   int32_t off_batch, off_counts, off_starts, off_items;
+  uint32_t fingerprint;     // of the problem of this call
+  int32_t rows;             // query rows (B * S1, or T1)
 };
 
 // Layout / dtype codes as in li.h.
@@ -117,6 +126,33 @@ struct GatherArgs {
 };
 constexpr int kGatherRows = 64;          // selected rows per gather workgroup
 
+// li_grad_kl: the backward of the indexer fused with its KL loss.
+struct GradArgs {
+  const void* q;            // main attention: [rows, G, 128]
+  const void* k;            // [keys, 128]
+  const void* q_rope;       // [rows, G, 64] or NULL
+  const void* k_rope;       // [keys, 64] or NULL
+  const void* qi;           // indexer: [rows, Ni, 128]
+  const void* ki;           // [keys, 128]
+  const void* w;            // [rows, Ni]
+  const int32_t* sel;       // sparse_indices [rows, topk]
+  const float* smax;        // softmax_max [rows, G]
+  const float* ssum;        // softmax_sum [rows, G]
+  const int32_t* cu_q;      // TND: inclusive prefix sums, else NULL
+  const int32_t* cu_k;
+  float* d_qi;              // [rows, Ni, 128]
+  float* d_ki;              // [keys, 128]
+  float* d_w;               // [rows, Ni]
+  float* loss;              // [1]
+  float* loss_rows;         // workspace: [rows]
+  int64_t keys;
+  int32_t rows, batch, s1, s2, layout;
+  int32_t G, Ni, topk, topk_pad;
+  float scale;
+};
+constexpr int kGradWaves = 4;            // rows per workgroup of the backward row kernel
+constexpr int kGradTileBytes = 20480;    // per wave: index, main and rope key tiles
+
 // Launchers (defined in the .hip files); return the hipGetLastError() of the launch.
 hipError_t launch_metadata(const KArgs& a, int mode, hipStream_t s);
 hipError_t launch_gather(const KArgs& a, const GatherArgs& g, int64_t rows, hipStream_t s);
@@ -126,5 +162,6 @@ hipError_t launch_decode(const KArgs& a, int qk_dtype, int w_dtype, int mblocks,
                          int grid, hipStream_t s);
 hipError_t launch_select(const KArgs& a, int grid, size_t lds, hipStream_t s);
 size_t select_shared_bytes();   // LDS of the select kernel
+hipError_t launch_grad(const GradArgs& g, int qk_dtype, int w_dtype, bool rope, hipStream_t s);
 
 }  // namespace li

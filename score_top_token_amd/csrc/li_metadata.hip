@@ -253,6 +253,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
     hdr->magic = kMetaMagic;
     hdr->batch = B;
     hdr->max_items = a.max_items;
+    hdr->fingerprint = a.fingerprint;
   }
   __syncthreads();
 

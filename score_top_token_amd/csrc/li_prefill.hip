@@ -314,6 +314,7 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
 template <int QK, int MB, int WT, int KL, bool G>
 __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  if (!check_meta(a)) return;
   const int n_items = reinterpret_cast<const MetaHeader*>(a.meta)->n_items;
   if constexpr (!G) {
     if ((int)blockIdx.x < n_items) dense_item<QK, MB, WT, KL, G>(a, blockIdx.x, smem);
@@ -342,6 +343,7 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void stream_shared_kernel(KAr
   constexpr int TILE = kPipeKeys * M::RB;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
+  if (!check_meta(a)) return;
   const MetaHeader* hdr = reinterpret_cast<const MetaHeader*>(a.meta);
   if ((int)blockIdx.x >= hdr->n_items) return;
   const int4 item = reinterpret_cast<const int4*>(a.meta + a.off_items)[blockIdx.x];
@@ -530,6 +532,7 @@ __global__ __launch_bounds__(W * 64, 1) void stream_kernel(KArgs a) {
   constexpr int TILE = kPipeKeys * M::RB;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
+  if (!check_meta(a)) return;
   const MetaHeader* hdr = reinterpret_cast<const MetaHeader*>(a.meta);
   if ((int)blockIdx.x >= hdr->n_items) return;
   const int4 item = reinterpret_cast<const int4*>(a.meta + a.off_items)[blockIdx.x];

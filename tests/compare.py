@@ -51,8 +51,9 @@ def check_row(g_idx: np.ndarray, g_val, o_idx: np.ndarray, o_val: np.ndarray, n_
         assert np.all(np.isneginf(tail)), f"{where}: value padding is not -inf"
     o_set = dict(zip(o_idx[:n].tolist(), o_val[:n].astype(np.float64).tolist()))
     g_keys = g_idx[:n].tolist()
+    g_set = set(g_keys)
     extra = [s for s in g_keys if s not in o_set]
-    missing = [s for s in o_set if s not in set(g_keys)]
+    missing = [s for s in o_set if s not in g_set]
     ref = dict(o_set)
     for s in extra:
         ref[s] = float(score_of(s))

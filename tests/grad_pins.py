@@ -244,4 +244,27 @@ def pin_thread_count_invariance():
         assert np.array_equal(x, y)
 
 
+def pin_homogeneity():
+    # I is positively homogeneous of degree 1 in qi, in ki and in w separately
+    # (ReLU(c x) = c ReLU(x) for c >= 0), so Euler's identity gives
+    # <d_qi, qi> = <d_ki, ki> = <d_w, w> = sum over rows and entries of dI * I
+    inst = _small(10)
+    loss, dqi, dki, dw = grad.Bound(inst).backward(nthreads=2)
+    a = float((dqi * inst["qi"].numpy().reshape(dqi.shape)).sum())
+    b = float((dki * inst["ki"].numpy().reshape(dki.shape)).sum())
+    c = float((dw * inst["w"].numpy().reshape(dw.shape)).sum())
+    assert abs(a) > 1e-3
+    assert abs(a - b) <= 1e-9 * abs(a) and abs(a - c) <= 1e-9 * abs(a), (a, b, c)
+
+
+def pin_rows_subset_matches():
+    inst = _small(11)
+    ob = grad.Bound(inst)
+    loss, dqi, dki, dw = ob.backward(nthreads=2)
+    rows = [0, 5, 21, 39]
+    l2, q2, w2 = ob.backward_rows(rows)
+    assert np.array_equal(l2, loss[rows]) and np.array_equal(q2, dqi[rows])
+    assert np.array_equal(w2, dw[rows])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -29,6 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert binding.li_status_str(0) == "LI_OK"
+    assert binding.li_status_str(5) == "LI_ERR_METADATA_MISMATCH"
     assert binding.li_status_str(2) == "LI_ERR_UNSUPPORTED"
     assert binding.li_status_str(99) == "LI_UNKNOWN_STATUS"
 
@@ -87,7 +88,7 @@ def test_sizes_prefill_and_decode():
     p = binding.problem_for(synth.make("tiny", 0))
     st, mb = binding.li_metadata_size(p)
     st2, wb = binding.li_workspace_size(p)
-    assert st == OK and st2 == OK and mb > 256 and wb == 0
+    assert st == OK and st2 == OK and mb > 256 and wb == 256      # the status block only
     dec = synth.scaled_spec("decode", batch=4, len_lo=300, len_hi=900, block_size=64)
     inst = synth.make(dec, 0)
     pd = binding.problem_for(inst)
@@ -122,8 +123,9 @@ def test_forward_pointer_rules():
     p = base_problem()
     _, mb = binding.li_metadata_size(p)
     F = FAKE
+    _, wb0 = binding.li_workspace_size(p)
     args = dict(q=F, k=F, w=F, qd=None, kd=None, cq=None, ck=None, su=None, cr=None, bt=None,
-                off=None, meta=F, ws=None, wsb=0, idx=F, val=F)
+                off=None, meta=F, ws=F, wsb=wb0, idx=F, val=F)
 
     def call(prob=p, **over):
         a = dict(args)
@@ -137,6 +139,8 @@ def test_forward_pointer_rules():
     assert call(w=None) == INVALID
     assert call(meta=None) == INVALID
     assert call(idx=None) == INVALID
+    assert call(ws=None) == INVALID                       # the status block is always needed
+    assert call(wsb=wb0 - 1) == TOO_SMALL
     assert call(q=F + 2) == INVALID                       # q not 16-byte aligned
     assert call(qd=F) == INVALID                          # descales only with fp8
     assert call(bt=F) == INVALID                          # block_table only with PA
@@ -160,8 +164,9 @@ def test_empty_problem_launches_nothing():
     p = base_problem(batch=0)
     _, mb = binding.li_metadata_size(p)
     assert binding.li_metadata(p, None, None, None, None, FAKE, mb, None) == OK
+    _, wb = binding.li_workspace_size(p)
     assert binding.li_forward(p, FAKE, FAKE, FAKE, None, None, None, None, None, None, None,
-                              None, FAKE, None, 0, FAKE, None, None) == OK
+                              None, FAKE, FAKE, wb, FAKE, None, None) == OK
     tnd = base_problem(layout_q=1, layout_k=1, total_q=0, total_k=0, batch=3)
     _, mt = binding.li_metadata_size(tnd)
     assert binding.li_metadata(tnd, FAKE, FAKE, None, None, FAKE, mt, None) == OK
@@ -203,3 +208,4 @@ def test_gather_pointer_rules():
     assert call(prob=pa) == INVALID                        # PA needs block_table
     assert call(prob=pa, bt=F, stride=16) == INVALID       # stride below a block
     assert call(prob=base_problem(batch=0)) == OK          # nothing to gather
+

@@ -100,7 +100,9 @@ def compare_all(inst, rows=None, return_value=1, seed_rows=0):
     if rows is None:
         rows = np.arange(gi.shape[0])
     rows = np.asarray(rows, dtype=np.int64)
+    _say(f"    oracle on {len(rows)} rows ({ORACLE_THREADS} threads)")
     oi, ov = ob.forward(rows=rows, nthreads=ORACLE_THREADS)
+    _say("    comparing")
     if inst.get("output_idx_offset") is not None:
         per_row = np.repeat(inst["output_idx_offset"].numpy().astype(np.int64),
                             inst["seqlens_q"])[rows]
@@ -482,7 +484,7 @@ def full_size_rows(name, inst, seed):
         # and seeded random rows
         rows |= slot_rows(inst, items, grid, (0, 1), range(grid))
         later = range(2, -(-len(items) // grid))
-        rows |= slot_rows(inst, items, grid, later, range(0, grid, 4))
+        rows |= slot_rows(inst, items, grid, later, range(0, grid, 64))
         rows.update(rng.integers(0, total, 128).tolist())
         assert len(rows) >= 1024
     else:                                         # longfp8
@@ -501,10 +503,19 @@ def test_full_size_config(name, seed):
     compare_all(inst, rows=rows)
 
 
+def _by_index(idx, val):
+    """Each row's entries sorted by index (the order inside the valid prefix is
+    not part of the contract), values carried along as raw bits."""
+    order = np.argsort(idx, axis=1, kind="stable")
+    return np.take_along_axis(idx, order, 1), np.take_along_axis(val.view(np.uint32), order, 1)
+
+
 def test_determinism_across_splits():
     """A row's output does not depend on how the work was cut: the same
     sequences run in one batch (one decode segment length, one work list) and
-    each on its own (other segment lengths, other items) give bitwise equal rows."""
+    each on its own (other segment lengths, other items, and for the TND case
+    rows in LDS instead of the workspace) give the same index set per row with
+    bitwise equal values."""
     dec = synth.Spec(name="split_dec", batch=6, s1=2, n1=64, topk=300, layout_k="PA_BSND",
                      len_lo=1000, len_hi=30000, block_size=128, w_scale=0.125)
     inst = synth.make(dec, 31)
@@ -519,8 +530,8 @@ def test_determinism_across_splits():
                    q=inst["q"][b:b + 1].clone(), w=inst["w"][b:b + 1].clone(),
                    name=f"split_dec_b{b}")
         oi, ov = _gpu(one)
-        assert np.array_equal(oi, gi[b * nq:(b + 1) * nq]), b
-        assert np.array_equal(ov.view(np.uint32), gv[b * nq:(b + 1) * nq].view(np.uint32)), b
+        a, b_ = _by_index(oi, ov), _by_index(gi[b * nq:(b + 1) * nq], gv[b * nq:(b + 1) * nq])
+        assert np.array_equal(a[0], b_[0]) and np.array_equal(a[1], b_[1]), b
     # prefill: TND sequences alone and packed with others (rows in LDS and in the workspace)
     tnd = synth.Spec(name="split_tnd", batch=4, n1=64, topk=256, layout_q="TND",
                      layout_k="TND", fixed_lengths=[3000, 700, 5200, 64], w_scale=0.125)
@@ -537,5 +548,72 @@ def test_determinism_across_splits():
                    q=inst["q"][sl].clone(), k=inst["k"][sl].clone(), w=inst["w"][sl].clone(),
                    name=f"split_tnd_b{b}")
         oi, ov = _gpu(one)
-        assert np.array_equal(oi, gi[sl]), b
-        assert np.array_equal(ov.view(np.uint32), gv[sl].view(np.uint32)), b
+        a, b_ = _by_index(oi, ov), _by_index(gi[sl], gv[sl])
+        assert np.array_equal(a[0], b_[0]) and np.array_equal(a[1], b_[1]), b
+
+
+def _device_inputs(inst, dev):
+    g = {n: (inst[n].to(dev) if isinstance(inst.get(n), torch.Tensor) else None)
+         for n in ("q", "k", "w", "q_descale", "k_descale", "cu_seqlens_q", "cu_seqlens_k",
+                   "seqused_k", "block_table", "cmp_residual_k", "output_idx_offset")}
+    if inst["layout_k"] == "PA_BSND":
+        kc = inst["k"]
+        base = kc.as_strided((kc.shape[0], kc.stride(0)), (kc.stride(0), 1)).to(dev)
+        g["k"] = base.as_strided(kc.shape, kc.stride())
+    return g
+
+
+def _forward(p, g, meta):
+    st, wsb = binding.li_workspace_size(p)
+    assert st == 0
+    ws = torch.empty(wsb, dtype=torch.uint8, device=g["q"].device)
+    idx, val = binding.lightning_indexer(
+        p, g["q"], g["k"], g["w"], metadata=meta, q_descale=g["q_descale"],
+        k_descale=g["k_descale"], cu_seqlens_q=g["cu_seqlens_q"], cu_seqlens_k=g["cu_seqlens_k"],
+        seqused_k=g["seqused_k"], block_table=g["block_table"], workspace=ws)
+    return idx, val, binding.forward_status(ws)
+
+
+@pytest.mark.parametrize("spec", [
+    dict(batch=2, s1=300, s2=300, n1=16, topk=64),                      # rows in LDS
+    dict(batch=1, s1=20, s2=6000, n1=16, topk=64),                      # rows in the workspace
+    dict(batch=3, s1=1, n1=16, topk=64, layout_k="PA_BSND", len_lo=500, len_hi=3000,
+         block_size=64),                                                # decode
+])
+def test_metadata_of_another_problem(spec):
+    """Metadata built for another problem is refused on the device: the same batch
+    and lengths with another topk (so that every item read would stay in bounds even
+    without the check) give -1 / -inf everywhere and the mismatch status word, and
+    li_gather then writes zero rows; the matching call reports LI_OK."""
+    dev = torch.device("cuda")
+    inst = synth.make(synth.Spec(name="meta_mismatch", **spec), 40)
+    _say(f"[gpu] metadata mismatch {spec}")
+    g = _device_inputs(inst, dev)
+    p = binding.problem_for(inst, g["k"])
+    meta = binding.lightning_indexer_metadata(p, cu_seqlens_q=g["cu_seqlens_q"],
+                                              cu_seqlens_k=g["cu_seqlens_k"],
+                                              seqused_k=g["seqused_k"], device=dev)
+    idx, val, st = _forward(p, g, meta)
+    assert st == 0
+    ok_idx = idx.reshape(-1, p.topk)
+    assert (ok_idx[:, 0] >= 0).any()
+    p2 = binding.problem_for(dict(inst, topk=2 * p.topk), g["k"])
+    assert binding.li_metadata_size(p2)[1] == binding.li_metadata_size(p)[1]
+    idx2, val2, st2 = _forward(p2, g, meta)
+    assert st2 == 5 and binding.li_status_str(st2) == "LI_ERR_METADATA_MISMATCH"
+    assert (idx2 == -1).all() and torch.isneginf(val2).all()
+    # li_gather with the same foreign metadata: valid indices (from the matching
+    # call, so reads would stay in bounds) still give zero rows
+    sel = torch.cat([ok_idx, ok_idx], dim=1).clamp(min=0).contiguous()
+    kv = (torch.arange(int(inst["k"].numel()) // 128 * 16, device=dev) % 251 + 1).to(torch.uint8)
+    if inst["layout_k"] == "PA_BSND":
+        kv = kv.reshape(inst["k"].shape[0], inst["block_size"], 16)
+    else:
+        kv = kv.reshape(*inst["k"].shape[:-2], 16)
+    out = binding.gather_selected(p2, kv, sel, metadata=meta, block_table=g["block_table"])
+    torch.cuda.synchronize()
+    assert (out == 0).all()
+    out_ok = binding.gather_selected(p, kv, ok_idx.contiguous(), metadata=meta,
+                                     block_table=g["block_table"])
+    torch.cuda.synchronize()
+    assert (out_ok != 0).any()
