@@ -191,6 +191,31 @@ li_status li_forward(const li_problem* p, const void* q, const void* k, const vo
                      int32_t* sparse_indices, float* sparse_values, hipStream_t stream);
 
 /*
+ * li_forward without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and results as li_forward otherwise.  The kernels'
+ * scratch is one file-scope device array of 128 MiB per GPU (allocated with the
+ * library's code on that GPU and held until the process ends); the call makes no
+ * hipMalloc / hipFree and allocates nothing.  The current device's copy is looked
+ * up on the first call on that device (hipGetSymbolAddress), so the calling thread's
+ * current device must be the one `stream` belongs to.
+ *  - A problem whose li_workspace_size exceeds 128 MiB is rejected with
+ *    LI_ERR_WORKSPACE_TOO_SMALL before any HIP call (use li_forward for it).
+ *  - Every call on one GPU shares that GPU's array, which keeps the last call's
+ *    contents: calls that overlap on one GPU (other streams or threads) race and
+ *    must be serialised by the caller.  Nothing in it needs to start at zero.
+ *  - The status word of li_forward lives in that array; a metadata mismatch still
+ *    writes -1 / -inf into every output slot.
+ */
+li_status li_forward_noalloc(const li_problem* p, const void* q, const void* k, const void* w,
+                             const float* q_descale, const float* k_descale,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                             const int32_t* seqused_k, const int32_t* cmp_residual_k,
+                             const int32_t* block_table, const int32_t* output_idx_offset,
+                             const void* metadata, int32_t* sparse_indices, float* sparse_values,
+                             hipStream_t stream);
+
+/*
  * Gathers, for every query row, the key (or value) rows its top-k selected: the
  * step after the indexer, where sparse attention reads its selected keys
  * (aclnnSparseFlashAttentionGrad page, calculation formula: the selected key is

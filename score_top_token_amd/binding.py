@@ -27,8 +27,9 @@ DTYPE = {torch.bfloat16: 0, torch.float8_e4m3fn: 1, torch.float32: 2, torch.floa
 STATUS = {0: "LI_OK", 1: "LI_ERR_INVALID_ARGUMENT", 2: "LI_ERR_UNSUPPORTED",
           3: "LI_ERR_WORKSPACE_TOO_SMALL", 4: "LI_ERR_HIP", 5: "LI_ERR_METADATA_MISMATCH"}
 
-EXPORTED = ("li_metadata_size", "li_workspace_size", "li_metadata", "li_forward", "li_gather",
-            "li_grad_workspace_size", "li_grad_kl", "li_status_str")
+EXPORTED = ("li_metadata_size", "li_workspace_size", "li_metadata", "li_forward",
+            "li_forward_noalloc", "li_gather", "li_grad_workspace_size", "li_grad_kl",
+            "li_status_str")
 
 
 class Problem(ctypes.Structure):
@@ -84,6 +85,7 @@ def load():
         L.li_metadata.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
         L.li_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                  vp, vp]
+        L.li_forward_noalloc.argtypes = [P] + [vp] * 15
         L.li_gather.argtypes = [P, vp, ctypes.c_int32, ctypes.c_int64, vp, ctypes.c_int32, vp, vp,
                                 vp, vp]
         GP = ctypes.POINTER(GradProblem)
@@ -92,7 +94,7 @@ def load():
         L.li_status_str.argtypes = [ctypes.c_int]
         L.li_status_str.restype = ctypes.c_char_p
         for n in ("li_metadata_size", "li_workspace_size", "li_metadata", "li_forward",
-                  "li_gather", "li_grad_workspace_size", "li_grad_kl"):
+                  "li_forward_noalloc", "li_gather", "li_grad_workspace_size", "li_grad_kl"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -127,6 +129,15 @@ def li_forward(p: Problem, q, k, w, q_descale, k_descale, cu_seqlens_q, cu_seqle
                              cu_seqlens_k, seqused_k, cmp_residual_k, block_table,
                              output_idx_offset, metadata, workspace, workspace_bytes,
                              sparse_indices, sparse_values, stream)
+
+
+def li_forward_noalloc(p: Problem, q, k, w, q_descale, k_descale, cu_seqlens_q, cu_seqlens_k,
+                       seqused_k, cmp_residual_k, block_table, output_idx_offset, metadata,
+                       sparse_indices, sparse_values, stream) -> int:
+    return load().li_forward_noalloc(ctypes.byref(p), q, k, w, q_descale, k_descale, cu_seqlens_q,
+                                     cu_seqlens_k, seqused_k, cmp_residual_k, block_table,
+                                     output_idx_offset, metadata, sparse_indices, sparse_values,
+                                     stream)
 
 
 def li_gather(p: Problem, kv, row_bytes, kv_block_stride, sparse_indices, select_block,

@@ -4,6 +4,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
+
+#include <hip/hip_runtime.h>
 
 #include "li.h"
 #include "li_internal.h"
@@ -344,6 +347,35 @@ li_status forward_launch(const li_problem* p, const Plan& pl, const void* q, con
 
 }  // namespace
 
+// ---- the no-allocation entry point ------------------------------------------
+// Scratch of li_forward_noalloc: one array per GPU, held until the process ends.
+// In host code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // per device: the address of `scratch` there
+
+// The current device's copy of `scratch` (looked up on the first call per device).
+li_status device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LI_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return LI_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LI_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 li_status li_forward(const li_problem* p, const void* q, const void* k, const void* w,
@@ -363,6 +395,27 @@ li_status li_forward(const li_problem* p, const void* q, const void* k, const vo
   return forward_launch(p, pl, q, k, w, q_descale, k_descale, cu_seqlens_q, cu_seqlens_k,
                         seqused_k, cmp_residual_k, block_table, output_idx_offset, metadata,
                         workspace, sparse_indices, sparse_values, stream);
+}
+
+li_status li_forward_noalloc(const li_problem* p, const void* q, const void* k, const void* w,
+                             const float* q_descale, const float* k_descale,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                             const int32_t* seqused_k, const int32_t* cmp_residual_k,
+                             const int32_t* block_table, const int32_t* output_idx_offset,
+                             const void* metadata, int32_t* sparse_indices, float* sparse_values,
+                             hipStream_t stream) {
+  Plan pl;
+  li_status st = forward_checks(p, &pl, q, k, w, q_descale, k_descale, cu_seqlens_q, cu_seqlens_k,
+                                seqused_k, cmp_residual_k, block_table, metadata, sparse_indices);
+  if (st != LI_OK) return st;
+  if (pl.ws_bytes > kNoAllocScratchBytes) return LI_ERR_WORKSPACE_TOO_SMALL;
+  if (query_rows(p) == 0) return LI_OK;
+  void* ws = nullptr;
+  st = device_scratch(&ws);
+  if (st != LI_OK) return st;
+  return forward_launch(p, pl, q, k, w, q_descale, k_descale, cu_seqlens_q, cu_seqlens_k,
+                        seqused_k, cmp_residual_k, block_table, output_idx_offset, metadata, ws,
+                        sparse_indices, sparse_values, stream);
 }
 
 li_status li_gather(const li_problem* p, const void* kv, int32_t row_bytes, int64_t kv_block_stride,

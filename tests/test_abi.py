@@ -209,3 +209,20 @@ def test_gather_pointer_rules():
     assert call(prob=pa, bt=F, stride=16) == INVALID       # stride below a block
     assert call(prob=base_problem(batch=0)) == OK          # nothing to gather
 
+
+def test_noalloc_rejects_workspace_past_its_scratch():
+    # 2048 query rows of 20000 keys: workspace rows of 164 MB, past the 128 MiB
+    # scratch array of li_forward_noalloc -> rejected before any HIP call
+    p = base_problem(max_seqlen_q=2048, max_seqlen_k=20000, num_heads_q=64, topk=2048)
+    st, wsb = binding.li_workspace_size(p)
+    assert st == OK and wsb > (128 << 20)
+    F = FAKE
+    assert binding.li_forward_noalloc(p, F, F, F, None, None, None, None, None, None, None, None,
+                                      F, F, F, None) == TOO_SMALL
+    # argument checks come first, as in li_forward
+    assert binding.li_forward_noalloc(p, None, F, F, None, None, None, None, None, None, None,
+                                      None, F, F, F, None) == INVALID
+    # an empty problem is LI_OK without touching the device
+    e = base_problem(batch=0)
+    assert binding.li_forward_noalloc(e, F, F, F, None, None, None, None, None, None, None, None,
+                                      F, F, F, None) == OK
