@@ -223,7 +223,7 @@ def run_workload(name, args, dev, steps):
     # runs the first ~0.2 s of work up to 10% slower)
     t_w = time.perf_counter()
     done = 0
-    while done < args.warmup or time.perf_counter() - t_w < WARMUP_MIN_S:
+    while done < args.warmup or time.perf_counter() - t_w < args.min_warmup_s:
         if flush is not None:
             flush.sum()
         metadata()
@@ -308,7 +308,7 @@ def run_grad(name, args, dev, steps):
     run = lambda: binding.lightning_indexer_grad_kl(p, t, workspace=ws)
     t_w = time.perf_counter()
     done = 0
-    while done < args.warmup or time.perf_counter() - t_w < WARMUP_MIN_S:
+    while done < args.warmup or time.perf_counter() - t_w < args.min_warmup_s:
         run()
         done += 1
         if done % 8 == 0:
@@ -376,6 +376,8 @@ def main():
                     help="time this workload only (default: prefill as the headline, then "
                          "decode, varlen and longfp8 as sub-records)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--min-warmup-s", type=float, default=WARMUP_MIN_S,
+                    help="warm-up lasts at least this long (0 under a profiler)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -462,7 +464,7 @@ def bench_gather(args, dev):
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # read-evicts the caches
     t_w = time.perf_counter()
     done = 0
-    while done < args.warmup or time.perf_counter() - t_w < WARMUP_MIN_S:
+    while done < args.warmup or time.perf_counter() - t_w < args.min_warmup_s:
         flush.sum()
         gather()
         done += 1
