@@ -16,8 +16,8 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblightning_indexer.so")
-SOURCES = ["li_host.cpp", "li_metadata.hip", "li_prefill.hip", "li_decode.hip", "li_gather.hip",
-           "li_grad.hip"]
+SOURCES = ["li_prefill_bf16.hip", "li_prefill_fp16.hip", "li_prefill_fp8.hip", "li_host.cpp",
+           "li_metadata.hip", "li_prefill.hip", "li_decode.hip", "li_gather.hip", "li_grad.hip"]
 ARCH = os.environ.get("LI_OFFLOAD_ARCH", "gfx950")
 
 

@@ -116,9 +116,10 @@ li_status make_plan(const li_problem* p, Plan* pl) {
     pl->dcap = (int32_t)dcap;
     pl->lds_prefill = dense_lds;
     items = prefill_items(p, kDenseWaves);
-  } else if ((size_t)kDenseSlots * kDenseWaves * dcap * 4 <= kDenseGlobalMaxBytes) {
-    // rows too long for LDS: the same kernel with each row in a global workspace
-    // row, one per wave of a fixed grid of resident workgroups
+  } else if (p->max_seqlen_k <= kGlobalRowKeys) {
+    // rows too long for LDS: the same kernel with each row in a workspace row,
+    // one per wave of a fixed grid of resident workgroups (two per CU) walking
+    // the work list
     pl->mode = kModeDenseGlobal;
     pl->rows_per_item = kDenseWaves;
     items = prefill_items(p, kDenseWaves);
@@ -127,29 +128,20 @@ li_status make_plan(const li_problem* p, Plan* pl) {
     pl->ws_bytes = (size_t)pl->grid * kDenseWaves * dcap * 4;
     pl->lds_prefill = std::max(std::max(tiles, (size_t)kDenseWaves * kWideScratch), q_stage);
   } else {
-    // rows past the workspace cap (over 262144 keys): bounded candidate lists
-    pl->mode = kModeStream;
-    // Four rows per workgroup.  fp8: a 32-key K tile and the select scratch per
-    // wave, then the lists; otherwise two shared 32-key K tiles, the select
-    // scratch per wave, the lists.  Where four lists of a large topk do not fit
-    // the workgroup holds two rows, each wave with its own K tile.
-    const int k64 = (int)align_up(p->topk, 64);
-    const int need = k64 + 5 * kPipeKeys + 64;                        // room for a group of tiles
-    const size_t wave_fixed = (size_t)kPipeKeys * rb + kWaveScratch;
-    int waves = kStreamWaves;
-    size_t fixed = p->qk_dtype == LI_DT_FP8_E4M3 ? (size_t)kStreamWaves * wave_fixed
-                                                 : tiles + (size_t)kStreamWaves * kWaveScratch;
-    if ((int)((kLdsBudget - fixed) / (kStreamWaves * 8) / 64 * 64) < need) {
-      waves = kStreamWavesLarge;
-      fixed = (size_t)waves * wave_fixed;
-    }
-    const int fit = (int)((kLdsBudget - fixed) / (waves * 8) / 64 * 64);
-    const int cap = std::min(std::max(2 * k64, k64 + 512), fit);
-    if (cap < need) return LI_ERR_UNSUPPORTED;
-    pl->rows_per_item = waves;
-    items = prefill_items(p, waves);
+    // longer rows: the same grid; each row keeps its running top-k in its
+    // output slots and a candidate list in LDS (after the K tiles, the descale
+    // slots, the per-wave merge scratch and one int flag per wave)
+    pl->mode = kModeDenseList;
+    pl->rows_per_item = kDenseWaves;
+    items = prefill_items(p, kDenseWaves);
+    pl->grid = (int32_t)std::min<int64_t>(items, kDenseSlots);
+    const size_t fixed = tiles + (size_t)kDenseWaves * kListScratch + 16;
+    const int cap = (int)((kLdsBudget / 2 - fixed) / ((size_t)kDenseWaves * 8) / 64 * 64);
+    if (cap < 2 * kListRoom) return LI_ERR_UNSUPPORTED;
     pl->cap = cap;
-    pl->lds_prefill = fixed + (size_t)waves * cap * 8;
+    pl->lds_prefill = std::max(fixed + (size_t)kDenseWaves * cap * 8, q_stage);
+    // the running top-k's values when sparse_values is NULL: topk floats per resident wave
+    pl->ws_bytes = (size_t)pl->grid * kDenseWaves * p->topk * 4;
   }
   // the status block ahead of the kernels' scratch
   pl->ws_bytes += kStatusBytes;
@@ -334,7 +326,7 @@ li_status forward_launch(const li_problem* p, const Plan& pl, const void* q, con
                  : (p->block_size % 32 == 0 ? KL_PAGED_TILE : KL_PAGED);
   hipError_t e;
   if (pl.mode != kModeDecode) {
-    const int grid = pl.mode == kModeDenseGlobal ? pl.grid : pl.max_items;
+    const int grid = pl.mode == kModeDense ? pl.max_items : pl.grid;
     e = launch_prefill(a, pl.mode, qk, wt, pl.mblocks, kl, grid, pl.lds_prefill, stream);
   } else {
     e = launch_decode(a, qk, wt, pl.mblocks, kl,

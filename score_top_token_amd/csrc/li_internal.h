@@ -16,21 +16,24 @@ constexpr int kMaxTopkLarge = 8192;
 constexpr int kTileKeys = 64;           // decode: minimum keys per segment
 constexpr int kPipeKeys = 32;           // keys per K tile of the score pipelines (one MFMA column block)
 constexpr int kDenseWaves = 4;          // dense prefill: 4 query rows per workgroup, 2 workgroups / CU
-constexpr int kStreamWaves = 4;         // streaming prefill: 4 query rows per workgroup
-constexpr int kStreamWavesLarge = 2;    // streaming prefill, topk above 2048: 2 rows per workgroup
 constexpr int kDecodeMaxRows = 4;       // decode mode: at most this many query rows per batch
 constexpr int kDecodeWaves = 4;         // decode split kernel: waves per workgroup
 constexpr int kDecodeSegments = 1024;   // decode: key segments per pass (256 CUs x 4 waves)
 constexpr int kSelectThreads = 1024;    // decode-mode select kernel
 constexpr int kSelectBuckets = 2048;    // decode-mode select: histogram buckets
 constexpr size_t kLdsBudget = 160 * 1024;
-constexpr int kWaveScratch = 256 * 4 + 2 * 64 * 4;   // per-wave select scratch: histogram + gather
-constexpr int kDenseScratch = 512 * 4 + 2 * 64 * 4;  // dense kernel, rows in LDS: 512-bucket histogram + gather
-// dense kernel with rows in global memory: per-wave 2048-bucket histogram, gather
-// scratch and the 256-bucket histogram of the fallback select
-constexpr int kWideScratch = 2048 * 4 + 2 * 64 * 4 + 256 * 4;
+constexpr int kDenseScratch = 512 * 4 + 4 * 64 * 4;  // dense kernel, rows in LDS: 512-bucket histogram + gather
+constexpr int kListScratch = 320 * 4 + 4 * 64 * 4;   // dense kernel, candidate lists: merge-select scratch
+// dense kernel, rows in global memory: 2048-bucket histogram, gather / rank scratch, select histogram
+constexpr int kWideScratch = 2048 * 4 + 4 * 64 * 4 + 320 * 4;
+constexpr int kListRoom = 6 * kPipeKeys;  // candidate lists: free slots at the start of a pipeline run
+// Rows of up to this many keys keep their scores in a workspace row; longer
+// rows stream through candidate lists (the list's merges are wave-serial
+// selects over about k + cap entries, which pay off only for rows many times
+// longer than k; measured: 16K-key rows run 1.4x faster with workspace rows,
+// 128K-key rows 1.05x slower).
+constexpr int kGlobalRowKeys = 32768;
 constexpr int kDenseSlots = 512;         // resident dense workgroups: 2 per CU on 256 CUs
-constexpr size_t kDenseGlobalMaxBytes = size_t(1) << 31;   // workspace cap of that mode
 constexpr int kMetaMagic = 0x4C494D44;  // "LIMD"
 // The workspace starts with a status block: int32 word 0 receives the call's
 // status (0, or kStatusMetaMismatch when the metadata was built for another
@@ -38,7 +41,14 @@ constexpr int kMetaMagic = 0x4C494D44;  // "LIMD"
 constexpr size_t kStatusBytes = 256;
 constexpr int32_t kStatusMetaMismatch = 5;   // = LI_ERR_METADATA_MISMATCH
 
-enum Mode : int32_t { kModeDense = 0, kModeStream = 1, kModeDecode = 2, kModeDenseGlobal = 3 };
+// kModeDense: rows of at most `dcap` keys, every score kept in LDS;
+// kModeDenseGlobal: rows of up to kGlobalRowKeys keys, every score in a
+// workspace row; kModeDenseList: longer rows, a running top-k in the output
+// slots and an LDS candidate list per row; kModeDecode: a few query rows per
+// batch, split keys.
+enum Mode : int32_t { kModeDense = 0, kModeDenseGlobal = 1, kModeDecode = 2, kModeDenseList = 3 };
+// Row modes of the dense kernel (where a row's scores go), one per prefill mode.
+enum RowMode : int { kRowsLds = 0, kRowsGlobal = 1, kRowsList = 2 };
 
 // Metadata buffer layout (all int32 / int4 records, offsets in bytes):
 //   [0, 256)        header, see MetaHeader
@@ -65,7 +75,7 @@ struct Plan {
   int32_t max_items;
   int32_t rows_per_item;  // prefill: query rows per work item
   int32_t chunk;          // decode: minimum keys per segment
-  int32_t cap;            // streaming prefill: candidate slots per row
+  int32_t cap;            // candidate-list prefill: LDS list entries per row
   int32_t dcap;           // dense prefill: score slots per row
   int32_t mblocks;        // 1 (N1 <= 32) or 2 (N1 <= 64)
   size_t lds_prefill;     // dynamic LDS of the prefill kernel
@@ -75,7 +85,7 @@ struct Plan {
   size_t ws_bytes;
   int64_t ws_row_stride;  // decode: fp32 slots per (batch, row) score row
   int32_t seg_mm_stride;  // decode: segment (min, max) pairs per row
-  int32_t grid;           // dense rows in global memory: resident workgroups
+  int32_t grid;           // candidate-list prefill: resident workgroups
 };
 
 // Kernel argument block (passed by value).
@@ -92,7 +102,8 @@ struct KArgs {
   const int32_t* cmp_res;   // compressed keys under mask 3: residual original keys per batch
   const int32_t* idx_off;   // NULL or an index offset per batch
   unsigned char* meta;      // metadata base
-  float* ws;                // decode: dense score rows
+  float* ws;                // decode: dense score rows; candidate lists: top-k values
+                            // (when sparse_values is NULL), topk per resident wave
   float* seg_mm;            // decode: (min, max) score of each segment, seg_mm_stride pairs per row
   int32_t* out_idx;
   float* out_val;

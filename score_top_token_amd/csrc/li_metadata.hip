@@ -10,10 +10,10 @@
 //     the batch order rotated every round (workgroups are dealt to the 8 XCDs by
 //     index mod 8: without the rotation a batch count that is a multiple of 8
 //     would send every block of one batch to one XCD).  The dense kernel with
-//     rows in global memory walks the list with a stride of its fixed grid, so
-//     there the list is batch-major instead (longest sequence first, each from
-//     its last block): at any time every XCD works on one sequence, whose keys
-//     then stay in its L2;
+//     rows in global memory or in candidate lists walks the list with a stride
+//     of its fixed grid, so there the list is batch-major instead (longest
+//     sequence first, each from its last block): at any time every XCD works
+//     on one sequence, whose keys then stay in its L2;
 //   - decode mode: the visible keys of every query row cut into segments of one
 //     length, the shortest for which all rows together need at most
 //     kDecodeSegments segments; one item per segment.  The split kernel runs
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
     }
     n_slots = min((total + kXcdRound - 1) / kXcdRound * kXcdRound, a.max_items);
   }
-  if (small && mode == kModeDenseGlobal) {
+  if (small && (mode == kModeDenseGlobal || mode == kModeDenseList)) {
     // batches by query rows, descending (ties by index): items before batch b
     for (int b = tid; b < B; b += kMetaThreads) {
       const int len = s_bt[b].y;
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
       const int q0 = blk * a.rows_per_item;
       const int nrows = min(a.rows_per_item, rec.y - q0);
       int pos = u;
-      if (small && mode == kModeDenseGlobal) {
+      if (small && (mode == kModeDenseGlobal || mode == kModeDenseList)) {
         pos = s_gstart[b] + r;
       } else if (small) {
         // round-robin over batches, each batch walked from its last block.

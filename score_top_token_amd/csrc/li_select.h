@@ -113,44 +113,104 @@ __device__ inline void wave_rank_small(float f, uint32_t e, int m, int r, float&
   eb = (uint32_t)__shfl((int)e, src);
 }
 
-// Gathers the (<= kSelSmall) candidates selected by `in(p)` into lane order via
-// the wave's LDS scratch (kSelSmall floats + kSelSmall u32), ascending position.
-template <class Pred>
-__device__ inline int wave_gather(const float* vals, const uint32_t* idx, int n, float* sf,
-                                  uint32_t* se, Pred in, float& cf, uint32_t& ce) {
+constexpr int kRowUnroll = 16;
+
+// f(p, valid, v) over vals[0, n) in index order, in batches of kRowUnroll
+// rounds of 64 entries, lane l holding entry p = batch start + 64 u + l.  The
+// batch's loads are issued together, and f is called for every round of the
+// batch, with no branch around it, so that the rounds' work can interleave:
+// lanes past n get valid = false (their load re-reads entry n - 1).  Calls are
+// wave-uniform (f may ballot).
+template <class F>
+__device__ __forceinline__ void row_pass(const float* vals, int n, F f) {
+  const int l = lane_id();
+  for (int p0 = 0; p0 < n; p0 += 64 * kRowUnroll) {
+    float v[kRowUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int p = p0 + 64 * u + l;
+      v[u] = vals[p < n ? p : n - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int p = p0 + 64 * u + l;
+      f(p, p < n, v[u]);
+    }
+  }
+}
+
+// Views of the entries a select runs over: pass(f) calls f(p, valid, v) for
+// every entry p in order, lane by lane (wave-uniform calls, so f may ballot),
+// with kRowUnroll loads in flight per lane; key(p) is entry p's key.
+// ArrayView: one array (idx == nullptr: the key of entry p is p).
+// MemUnionView: a row's running top-k, entries [0, n0), followed by its
+// candidate list, entries n0 + [0, n1).  Either way keys ascend with p.
+struct ArrayView {
+  const float* v;
+  const uint32_t* i;
+  int n;
+  __device__ uint32_t key(int p) const { return i ? i[p] : (uint32_t)p; }
+  template <class F>
+  __device__ __forceinline__ void pass(F f) const {
+    row_pass(v, n, f);
+  }
+};
+struct MemUnionView {
+  const float* v0;
+  const uint32_t* i0;
+  int n0;
+  const float* v1;
+  const uint32_t* i1;
+  int n1;
+  __device__ uint32_t key(int p) const { return p < n0 ? i0[p] : i1[p - n0]; }
+  template <class F>
+  __device__ __forceinline__ void pass(F f) const {
+    row_pass(v0, n0, f);
+    row_pass(v1, n1, [&](int p, bool valid, float x) __attribute__((always_inline)) {
+      f(n0 + p, valid, x);
+    });
+  }
+};
+
+// Gathers the (<= kSelSmall) candidates selected by `in(f)` into lane order
+// via the wave's LDS scratch (2 kSelSmall floats + 2 kSelSmall u32; a lane
+// with nothing to write stores to its own slot of the upper halves, so no
+// branch splits the rounds), ascending position.  The pass records positions;
+// the keys are read afterwards, all at once (a key in memory is a round trip).
+template <class View, class Pred>
+__device__ inline int wave_gather(const View& vw, float* sf, uint32_t* se, Pred in, float& cf,
+                                  uint32_t& ce) {
   const int l = lane_id();
   int got = 0;
-  for (int p0 = 0; p0 < n; p0 += 64) {
-    const int p = p0 + l;
-    const float f = p < n ? vals[p] : 0.0f;
-    const bool take = p < n && in(f);
+  vw.pass([&](int p, bool valid, float f) __attribute__((always_inline)) {
+    const bool take = valid && in(f);
     const uint64_t m = ballot(take);
-    if (take) {
-      const int slot = got + mbcnt(m);
-      if (slot < kSelSmall) {
-        sf[slot] = f;
-        se[slot] = idx ? idx[p] : (uint32_t)p;
-      }
-    }
+    const int slot = got + mbcnt(m);
+    const int at = (take & (slot < kSelSmall)) ? slot : kSelSmall + l;
+    sf[at] = f;
+    se[at] = (uint32_t)p;
     got += __popcll(m);
-  }
+  });
   wave_sync();
   cf = l < got ? sf[l] : 0.0f;
-  ce = l < got ? se[l] : 0u;
+  const int pos = l < got ? (int)se[l] : 0;
+  ce = l < got ? vw.key(pos) : 0u;
   wave_sync();
   return got;
 }
 
-// Wave-level k-th element of vals[0, n) (LDS).  idx == nullptr: the index of
-// entry p is p (a dense score row); otherwise idx[p] (the list is in ascending
-// index order).  lo / hi: bounds of the n values (min and max for speed).
-// hist: 256 u32 and scr: 2 * kSelSmall words of LDS private to the wave.
-// 1 <= k <= n.
-__device__ inline void wave_kth(const float* vals, const uint32_t* idx, int n, int k, float lo,
-                                float hi, uint32_t* hist, uint32_t* scr, float& fb, uint32_t& eb) {
+// Wave-level k-th element of the view's entries [0, n): keys ascend with the
+// position (a dense row, a list in key order, or two such ranges in order).
+// lo / hi: bounds of the n values (lo <= every value <= hi; the min and max
+// for speed).  hist: 256 + 64 u32 (a lane past the end counts into its own
+// slot of the last 64, so no branch splits the rounds) and scr: 4 * kSelSmall
+// words of LDS private to the wave.  1 <= k <= n.
+template <class View>
+__device__ inline void wave_kth_view(const View& vw, int n, int k, float lo, float hi,
+                                     uint32_t* hist, uint32_t* scr, float& fb, uint32_t& eb) {
   const int l = lane_id();
   float* sf = reinterpret_cast<float*>(scr);
-  uint32_t* se = scr + kSelSmall;
+  uint32_t* se = scr + 2 * kSelSmall;
   int r = k;
   uint32_t ulo, uhi;
   // ---- pass 1: linear value buckets ------------------------------------
@@ -158,7 +218,9 @@ __device__ inline void wave_kth(const float* vals, const uint32_t* idx, int n, i
     const FBucket fbk(lo, hi);
     for (int x = l; x < 256; x += 64) hist[x] = 0;
     wave_sync();
-    for (int p = l; p < n; p += 64) atomicAdd(&hist[fbk(vals[p])], 1u);
+    vw.pass([&](int, bool valid, float f) __attribute__((always_inline)) {
+      atomicAdd(&hist[valid ? fbk(f) : 256u + l], 1u);
+    });
     wave_sync();
     int B, above, cnt;
     wave_find_bucket(hist, r, B, above, cnt);
@@ -168,20 +230,18 @@ __device__ inline void wave_kth(const float* vals, const uint32_t* idx, int n, i
     if (cnt <= kSelSmall) {
       float cf;
       uint32_t ce;
-      const int got = wave_gather(vals, idx, n, sf, se, [&](float f) { return fbk(f) == ub; }, cf, ce);
+      const int got = wave_gather(vw, sf, se, [&](float f) { return fbk(f) == ub; }, cf, ce);
       wave_rank_small(cf, ce, got, r, fb, eb);
       return;
     }
     // key range of the chosen bucket, then continue on u32 keys
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-    for (int p = l; p < n; p += 64) {
-      const float f = vals[p];
-      if (fbk(f) == ub) {
-        const uint32_t u = f2key(f);
-        mn = min(mn, u);
-        mx = max(mx, u);
-      }
-    }
+    vw.pass([&](int, bool valid, float f) __attribute__((always_inline)) {
+      const bool in = valid && fbk(f) == ub;
+      const uint32_t u = f2key(f);
+      mn = in ? min(mn, u) : mn;
+      mx = in ? max(mx, u) : mx;
+    });
     ulo = wave_min_u(mn);
     uhi = wave_max_u(mx);
   } else {
@@ -190,34 +250,33 @@ __device__ inline void wave_kth(const float* vals, const uint32_t* idx, int n, i
   // ---- exact passes on u32 keys ------------------------------------------
   for (;;) {
     if (ulo == uhi) {
-      // every remaining candidate equals this key: the r-th of them in index order
+      // every remaining candidate equals this key: the r-th of them in key order
       fb = key2f(ulo);
       eb = 0;
       int seen = 0;
-      for (int p0 = 0; p0 < n; p0 += 64) {
-        const int p = p0 + l;
-        const bool eq = p < n && f2key(vals[p]) == ulo;
+      vw.pass([&](int p, bool valid, float f) __attribute__((always_inline)) {
+        const bool eq = valid && f2key(f) == ulo;
         const uint64_t m = ballot(eq);
         const int c = __popcll(m);
-        if (seen + c >= r) {
+        if (seen < r && seen + c >= r) {           // uniform: the round that holds it
           const bool hit = eq && seen + mbcnt(m) == r - 1;
           const uint64_t who = ballot(hit);
           const int src = who ? (int)__builtin_ctzll(who) : 0;
-          const uint32_t e = idx ? (p < n ? idx[p] : 0u) : (uint32_t)p;
+          const uint32_t e = hit ? vw.key(p) : 0u;
           eb = (uint32_t)__shfl((int)e, src);
-          return;
         }
         seen += c;
-      }
+      });
       return;
     }
     const UBucket ubk(ulo, uhi);
     for (int x = l; x < 256; x += 64) hist[x] = 0;
     wave_sync();
-    for (int p = l; p < n; p += 64) {
-      const uint32_t u = f2key(vals[p]);
-      if (u >= ulo && u <= uhi) atomicAdd(&hist[ubk(u)], 1u);
-    }
+    vw.pass([&](int, bool valid, float f) __attribute__((always_inline)) {
+      const uint32_t u = f2key(f);
+      const bool in = valid && u >= ulo && u <= uhi;
+      atomicAdd(&hist[in ? ubk(u) : 256u + l], 1u);
+    });
     wave_sync();
     int B, above, cnt;
     wave_find_bucket(hist, r, B, above, cnt);
@@ -229,7 +288,7 @@ __device__ inline void wave_kth(const float* vals, const uint32_t* idx, int n, i
     if (cnt <= kSelSmall && nlo != nhi) {
       float cf;
       uint32_t ce;
-      const int got = wave_gather(vals, idx, n, sf, se, [&](float f) {
+      const int got = wave_gather(vw, sf, se, [&](float f) {
         const uint32_t u = f2key(f);
         return u >= nlo && u <= nhi;
       }, cf, ce);
@@ -241,15 +300,20 @@ __device__ inline void wave_kth(const float* vals, const uint32_t* idx, int n, i
   }
 }
 
+// wave_kth_view over one array: idx == nullptr means the key of entry p is p.
+__device__ inline void wave_kth(const float* vals, const uint32_t* idx, int n, int k, float lo,
+                                float hi, uint32_t* hist, uint32_t* scr, float& fb, uint32_t& eb) {
+  wave_kth_view(ArrayView{vals, idx, n}, n, k, lo, hi, hist, scr, fb, eb);
+}
+
 // ---------------------------------------------------------------------------
-// Two-pass top-k of a dense score row (one wave per row), in global memory or
-// in LDS.  Each pass keeps kRowUnroll loads in flight per lane (for a global
+// Two-pass top-k of a dense score row (one wave per row), in LDS or in global
+// memory.  Each pass keeps kRowUnroll loads in flight per lane (for a global
 // row every load is an L2 round trip); one histogram of NB linear buckets
 // usually leaves at most kSelSmall values in the bucket of the k-th element:
-// kWideBuckets for rows of up to 262144 keys in global memory, kLdsBuckets for
-// rows of up to 4096 keys in LDS.
+// kLdsBuckets for rows of up to 4096 keys in LDS, kWideBuckets for longer rows
+// in global memory.
 // ---------------------------------------------------------------------------
-constexpr int kRowUnroll = 16;
 constexpr int kWideBuckets = 2048;
 constexpr int kLdsBuckets = 512;
 
@@ -270,27 +334,6 @@ struct FBucketN {
     return (uint32_t)__builtin_amdgcn_fmed3f(fmaf(f, a, c), 0.0f, (float)(NB - 1));
   }
 };
-
-// f(p, valid, v) over vals[0, n) (n >= 1) in index order, kRowUnroll * 64
-// entries per round, lane l holding entry p = round start + 64 u + l.  Calls
-// are wave-uniform (f may ballot); lanes past n get valid = false.
-template <class F>
-__device__ __forceinline__ void row_pass(const float* vals, int n, F f) {
-  const int l = lane_id();
-  for (int p0 = 0; p0 < n; p0 += 64 * kRowUnroll) {
-    float v[kRowUnroll];
-#pragma unroll
-    for (int u = 0; u < kRowUnroll; ++u) {
-      const int p = p0 + 64 * u + l;
-      v[u] = vals[p < n ? p : n - 1];
-    }
-#pragma unroll
-    for (int u = 0; u < kRowUnroll; ++u) {
-      const int p = p0 + 64 * u + l;
-      if (p0 + 64 * u < n) f(p, p < n, v[u]);
-    }
-  }
-}
 
 // wave_find_bucket over NB counts (lane l owns buckets NB/64 * l .. NB/64 * (l+1) - 1).
 template <int NB>
@@ -401,9 +444,9 @@ __device__ __forceinline__ bool wave_topk_row(const float* vals, int n, int k, f
   return true;
 }
 
-// The same, out of line: where the score loop already holds most registers
-// (rows in a global workspace), a call keeps the select's registers out of
-// the loop's allocation.
+// The same, out of line: the score loop around it already holds most
+// registers (rows in global memory), and a call keeps the select's registers
+// out of that allocation.
 template <int NB>
 __device__ __noinline__ bool wave_topk_row_call(const float* vals, int n, int k, float lo, float hi,
                                                 uint32_t* hist, uint32_t* scr, int32_t* oi,

@@ -211,9 +211,10 @@ def test_gather_pointer_rules():
 
 
 def test_noalloc_rejects_workspace_past_its_scratch():
-    # 2048 query rows of 20000 keys: workspace rows of 164 MB, past the 128 MiB
-    # scratch array of li_forward_noalloc -> rejected before any HIP call
-    p = base_problem(max_seqlen_q=2048, max_seqlen_k=20000, num_heads_q=64, topk=2048)
+    # 64 sequences of 4 query rows and 200000 keys: decode score rows of 205 MB,
+    # past the 128 MiB scratch array of li_forward_noalloc -> rejected before any
+    # HIP call
+    p = base_problem(batch=64, max_seqlen_q=4, max_seqlen_k=200000, num_heads_q=64, topk=2048)
     st, wsb = binding.li_workspace_size(p)
     assert st == OK and wsb > (128 << 20)
     F = FAKE

@@ -6,9 +6,10 @@ padding, values within 1e-2 * max(1, |I|), index sets equal up to swaps at the
 k-th score).  Small cases are compared on every row.  The five full-size
 workloads run at seeds 0, 1 and 2: prefill, decode and the tiny case on every
 row; varlen and longfp8 on stratified rows (first / last rows of every sequence,
-rows around |V| = k, rows of the items every grid slot of the global-row kernel
-runs in its first and later rounds, evenly spaced and seeded random rows), and
-structurally on every row.
+rows around |V| = k, rows of the items every grid slot of the persistent
+kernels (rows in workspace rows or in candidate lists) runs in its first and
+later rounds, evenly spaced and seeded random rows), and structurally on every
+row.
 """
 from __future__ import annotations
 
@@ -154,8 +155,8 @@ SMALL = {
                                             w_scale=0.35)),
     "decode_long_rows": (None, 22, dict(batch=2, s1=1, s2=40000, n1=16, topk=512,
                                         w_scale=0.25)),
-    # topk above 2048 (3072 .. 8192 in steps of 1024): dense rows, the 4-row
-    # streaming kernel, the 2-row streaming kernel (bf16 and fp8) and decode
+    # topk above 2048 (3072 .. 8192 in steps of 1024): rows past the LDS rows
+    # (workspace rows, bf16 and fp8) and decode
     "k8192_dense": (None, 23, dict(batch=1, s1=40, s2=9000, n1=64, topk=8192, w_scale=0.125)),
     "k3072_stream": (None, 24, dict(batch=1, s1=30, s2=12000, n1=64, topk=3072, w_scale=0.125)),
     "k8192_stream": (None, 25, dict(batch=1, s1=20, s2=20000, n1=64, topk=8192, w_scale=0.125)),
@@ -164,7 +165,7 @@ SMALL = {
     "k8192_decode": (None, 27, dict(batch=4, s1=1, n1=64, topk=8192, layout_k="PA_BSND",
                                     len_lo=5000, len_hi=20000, block_size=128, w_scale=0.125)),
     # compressed keys (cmp_ratio): the pages' example (130 original keys -> 32 with
-    # residual 2), a longer dense case, the streaming kernel, TND with per-sequence
+    # residual 2), a longer dense case, workspace rows, TND with per-sequence
     # residuals, decode rows with compression; output index offsets on every path
     "cmp_pages_example": (None, 28, dict(batch=2, s1=64, s2=32, n1=16, topk=32,
                                          qk_dtype="fp16", w_dtype="fp32", cmp_ratio=4,
@@ -182,8 +183,8 @@ SMALL = {
                                         idx_offset_max=1 << 20)),
     "idx_offset_stream": (None, 34, dict(batch=1, s1=40, s2=11000, n1=64, topk=512,
                                          idx_offset_max=1 << 20, w_scale=0.125)),
-    # rows past 262144 keys: the streaming kernels (bf16 / fp16 shared tiles, fp8
-    # per wave, and two rows per workgroup at topk 8192)
+    # rows past 262144 keys through candidate lists (bf16, fp8, fp16 at topk
+    # 8192: many merges per row, the top-k larger than the list)
     "stream_long_bf16": (None, 36, dict(batch=1, s1=6, s2=270000, n1=8, topk=300,
                                         idx_offset_max=1000)),
     "stream_long_fp8": (None, 37, dict(batch=1, s1=5, s2=263000, n1=16, topk=512,
@@ -197,8 +198,8 @@ SMALL = {
     "idx_offset_decode": (None, 35, dict(batch=6, s1=1, n1=64, topk=200, layout_k="PA_BSND",
                                          len_lo=100, len_hi=4000, block_size=128,
                                          idx_offset_max=1 << 20, w_scale=0.125)),
-    # fp8 keys with rows in the workspace (tiles through LDS in pairs): odd and even
-    # tile counts, and TND items of 1-2 tiles next to long ones
+    # fp8 keys with rows in the workspace: odd and even tile counts, and TND
+    # items of 1-2 tiles next to long ones
     "fp8_global_rows_odd": (None, 44, dict(batch=1, s1=70, s2=7000, n1=64, topk=300,
                                            qk_dtype="fp8", w_scale=0.125)),
     "fp8_global_rows_even_mask0": (None, 45, dict(batch=1, s1=37, s2=6016, n1=32, topk=500,
@@ -212,6 +213,22 @@ SMALL = {
     "scores_huge_global": (None, 42, dict(batch=1, s1=20, s2=6000, n1=16, topk=300, w_scale=1e25)),
     "scores_huge_decode": (None, 43, dict(batch=3, s1=1, n1=16, topk=100, layout_k="PA_BSND",
                                           len_lo=500, len_hi=3000, block_size=64, w_scale=1e25)),
+    # rows past 32768 keys: candidate lists.  bf16 at topk 2048 (the top-k larger
+    # than the list), fp8 TND items of 8-24 rows, fp16 keys in 64-key pages at
+    # topk 4096, per-key pages of 16 keys, compressed keys, index offsets
+    "list_bf16_k2048": (None, 47, dict(batch=1, s1=12, s2=40000, n1=64, topk=2048,
+                                       w_scale=0.125)),
+    "list_fp8_tnd": (None, 48, dict(batch=3, n1=16, topk=512, layout_q="TND", layout_k="TND",
+                                    len_lo=8, len_hi=24, kv_extra=36000, qk_dtype="fp8")),
+    "list_fp16_paged_k4096": (None, 49, dict(batch=2, s1=8, n1=32, topk=4096, layout_k="PA_BSND",
+                                             len_lo=33000, len_hi=40000, block_size=64,
+                                             qk_dtype="fp16", w_dtype="fp32")),
+    "list_paged_bs16": (None, 50, dict(batch=1, s1=8, n1=8, topk=256, layout_k="PA_BSND",
+                                       len_lo=34000, len_hi=36000, block_size=16)),
+    "list_cmp": (None, 51, dict(batch=1, s1=16, s2=36000, n1=16, topk=700, cmp_ratio=2,
+                                w_scale=0.25)),
+    "list_idx_offset": (None, 52, dict(batch=1, s1=8, s2=34000, n1=8, topk=1000,
+                                       idx_offset_max=1 << 20)),
 }
 
 
@@ -231,8 +248,8 @@ def test_return_value_zero_gives_same_indices():
     assert np.array_equal(gi0, gi1)
 
 
-# (S1, S2): rows in LDS, and rows long enough for the workspace rows of the dense kernel
-@pytest.mark.parametrize("s1,s2", [(300, 300), (40, 6000)])
+# (S1, S2): rows in LDS, workspace rows, and candidate lists (ties across merges)
+@pytest.mark.parametrize("s1,s2", [(300, 300), (40, 6000), (8, 40000)])
 def test_all_zero_scores_pick_smallest_indices(s1, s2):
     topk = 50
     q = torch.zeros(1, s1, 8, 128).bfloat16()
@@ -302,8 +319,8 @@ def test_paged_equals_contiguous():
     assert np.array_equal(gi, ri) and np.array_equal(gv, rv)
 
 
-# (S1, S2): decode (S1 <= 4 query rows), the dense kernel with rows in LDS, with
-# rows in the workspace, and the streaming kernel (rows past 262144 keys)
+# (S1, S2): decode (S1 <= 4 query rows), the dense kernel with rows in LDS, and
+# the list kernel (rows too long for LDS), with one row past 262144 keys
 @pytest.mark.parametrize("s1,s2", [(3, 300), (8, 300), (8, 12000), (8, 270000)])
 def test_negative_infinite_scores(s1, s2):
     """Scores of -inf (from infinite inputs) still fill the top-k: ties broken by
@@ -410,7 +427,7 @@ def test_prefill_work_list(spec):
     blocks of a single batch only."""
     inst = synth.make(synth.Spec(name="wlp", **spec), 3)
     hdr, items = _meta_items(inst)
-    assert hdr[1] in (0, 1, 3)                            # dense, streaming, dense with global rows
+    assert hdr[1] in (0, 1, 3)                            # rows in LDS, workspace rows, lists
     rows = 4
     want = set()
     for b in range(spec["batch"]):
@@ -478,7 +495,7 @@ def full_size_rows(name, inst, seed):
     rng = np.random.default_rng(1000 + seed)
     rows = strata_rows(inst)
     _, items = _meta_items(inst)
-    grid = min(len(items), 512)                   # resident slots of the global-row kernel
+    grid = min(len(items), 512)                   # resident slots of the list kernel
     if name == "varlen":
         # every slot in its first two rounds, every 4th slot in every later round,
         # and seeded random rows
