@@ -12,8 +12,8 @@
  *   2. visible keys: mask_mode 0 = all keys of the batch; mask_mode 3 =
  *      rightDownCausal, the lower triangle anchored at the bottom-right corner
  *      (npu_lightning_indexer_pto page, sparse_mode), read as
- *      s <= i + S2_b - S1_b, diagonal included ("the current token and all
- *      preceding tokens", lightning_indexer page, Function step 2).
+ *      s <= i + S2_b - S1_b, diagonal included (a token sees itself and the
+ *      tokens before it: lightning_indexer page, Function step 2).
  *      Compressed keys (cmp_ratio r > 1, lightning_indexer page, parameters and
  *      Example): key j stands for the r original positions j*r .. j*r + r - 1,
  *      the batch has S2_b*r + cmp_residual_k[b] original keys (the residual ones

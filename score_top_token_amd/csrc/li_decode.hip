@@ -321,34 +321,8 @@ __device__ inline void block_find_bucket(SelShared& sh, int r) {
   __syncthreads();
 }
 
-// linear value bucket in [0, kNB), monotone in f (one fused multiply-add, a
-// median-of-three clamp and a conversion)
-struct FBucketN {
-  float a, c;
-  __device__ FBucketN(float lo, float hi) {
-    const float lo2 = lo * 0.5f;
-    const float scale = fminf((float)kNB / (hi * 0.5f - lo2), 3.0e38f);
-    a = 0.5f * scale;
-    c = -lo2 * scale;
-  }
-  __device__ uint32_t operator()(float f) const {
-    return (uint32_t)__builtin_amdgcn_fmed3f(fmaf(f, a, c), 0.0f, (float)(kNB - 1));
-  }
-};
-
-struct UBucketN {
-  uint32_t ulo;
-  int shift;
-  __device__ UBucketN(uint32_t lo, uint32_t hi) : ulo(lo) {
-    const uint32_t span = hi - lo;
-    const int bits = span ? 32 - __clz(span) : 0;
-    shift = bits > 11 ? bits - 11 : 0;
-  }
-  __device__ uint32_t operator()(uint32_t u) const {
-    const uint32_t b = (u - ulo) >> shift;
-    return b > (uint32_t)(kNB - 1) ? (uint32_t)(kNB - 1) : b;
-  }
-};
+typedef LinBucket<kNB> FBucketN;     // linear value buckets (li_bucket.h)
+typedef KeyBucket<kNB> UBucketN;     // u32 key buckets of the refining passes
 
 // gathers the (<= kSelSmall) candidates with in(f) into sh.cand_*, then wave 0
 // ranks them; the k-th element lands in sh.misc[4..5].  Every element with

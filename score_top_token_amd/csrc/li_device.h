@@ -1,11 +1,12 @@
 // Device helpers for the gfx950 Lightning Indexer kernels: MFMA operand types,
-// the d-permutation shared by the Q (A) and K (B) operands, the fp32 -> ordered
-// u32 key map, and wave-level primitives.
+// the d-permutation shared by the Q (A) and K (B) operands and wave-level
+// primitives (the fp32 -> ordered u32 key map lives in li_bucket.h).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "li_bucket.h"
 #include "li_internal.h"
 
 namespace li {
@@ -124,22 +125,6 @@ __device__ inline typename Mma<QK>::frag load_frag_lds(const unsigned char* tile
 // in element r (0..15), row 8 * (r / 4) + 4 * (l / 32) + (r % 4).
 // ---------------------------------------------------------------------------
 __device__ inline int acc_row(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
-
-// ---------------------------------------------------------------------------
-// fp32 <-> order-preserving u32: a > b as floats  <=>  key(a) > key(b) as u32.
-// -0 is folded to +0 first.  Every finite value maps above 0x007FFFFF, so the
-// key 0 never belongs to a real score.
-// ---------------------------------------------------------------------------
-__device__ inline uint32_t f2key(float f) {
-  if (f == 0.0f) f = 0.0f;
-  uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ inline float key2f(uint32_t u) {
-  uint32_t v = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
-  return __uint_as_float(v);
-}
 
 // ---------------------------------------------------------------------------
 // Wave helpers (wave64)

@@ -59,8 +59,10 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(KArgs a, GatherA
       if (e < total) {
         const int j = j0 + e / chunks, c = e - (e / chunks) * chunks;
         const int sel = idx[j / g.sel];
-        const int s = sel * g.sel + (j - (j / g.sel) * g.sel);
-        if (sel >= 0 && s < br.w) {
+        // in 64 bits: an index far out of range must not wrap into the row
+        const int64_t s64 = (int64_t)sel * g.sel + (j - (j / g.sel) * g.sel);
+        if (sel >= 0 && s64 < br.w) {
+          const int s = (int)s64;
           const unsigned char* src;
           if (a.layout_k == L_PA) {
             int blk, slot;

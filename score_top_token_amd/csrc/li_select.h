@@ -42,34 +42,8 @@ __device__ inline uint32_t wave_max_u(uint32_t v) {
   return v;
 }
 
-// Linear value bucket in [0, 255]; halving first keeps (hi - lo) finite.
-struct FBucket {
-  float lo2, scale;
-  __device__ FBucket(float lo, float hi) {
-    lo2 = lo * 0.5f;
-    const float d = hi * 0.5f - lo2;
-    scale = fminf(256.0f / d, 3.0e38f);
-  }
-  __device__ uint32_t operator()(float f) const {
-    const float x = fminf((f * 0.5f - lo2) * scale, 255.0f);
-    return (uint32_t)fmaxf(x, 0.0f);
-  }
-};
-
-// Bucket of u32 keys in [ulo, uhi]: (u - ulo) >> shift, at most 255.
-struct UBucket {
-  uint32_t ulo;
-  int shift;
-  __device__ UBucket(uint32_t lo, uint32_t hi) : ulo(lo) {
-    const uint32_t span = hi - lo;
-    const int bits = span ? 32 - __clz(span) : 0;
-    shift = bits > 8 ? bits - 8 : 0;
-  }
-  __device__ uint32_t operator()(uint32_t u) const {
-    const uint32_t b = (u - ulo) >> shift;
-    return b > 255u ? 255u : b;
-  }
-};
+typedef LinBucket<256> FBucket;      // linear value buckets of the select
+typedef KeyBucket<256> UBucket;      // u32 key buckets of its refining passes
 
 // Finds, from 256 bucket counts (lane l owns buckets 4l..4l+3), the bucket that
 // holds the element of rank r (1-based) counted from the top.  Returns the
@@ -317,24 +291,6 @@ __device__ inline void wave_kth(const float* vals, const uint32_t* idx, int n, i
 constexpr int kWideBuckets = 2048;
 constexpr int kLdsBuckets = 512;
 
-// Linear value bucket in [0, NB): one fused multiply-add, a median-of-three
-// clamp and a conversion, each monotone in f, so a key of a higher bucket is
-// never below a key of a lower one.  Halving first keeps (hi - lo) finite; for f
-// in [lo, hi] the product f * a stays within a few units of NB * 2^24.
-template <int NB>
-struct FBucketN {
-  float a, c;
-  __device__ FBucketN(float lo, float hi) {
-    const float lo2 = lo * 0.5f;
-    const float scale = fminf((float)NB / (hi * 0.5f - lo2), 3.0e38f);
-    a = 0.5f * scale;
-    c = -lo2 * scale;
-  }
-  __device__ uint32_t operator()(float f) const {
-    return (uint32_t)__builtin_amdgcn_fmed3f(fmaf(f, a, c), 0.0f, (float)(NB - 1));
-  }
-};
-
 // wave_find_bucket over NB counts (lane l owns buckets NB/64 * l .. NB/64 * (l+1) - 1).
 template <int NB>
 __device__ inline void wave_find_bucket_n(const uint32_t* hist, int r, int& bkt, int& above,
@@ -383,7 +339,7 @@ __device__ __forceinline__ bool wave_topk_row(const float* vals, int n, int k, f
                                      int ioff) {
   if (!(lo < hi)) return false;
   const int l = lane_id();
-  const FBucketN<NB> fbk(lo, hi);
+  const LinBucket<NB> fbk(lo, hi);
   for (int x = l; x < NB; x += 64) hist[x] = 0;
   wave_sync();
   row_pass(vals, n, [&](int, bool valid, float f) __attribute__((always_inline)) {

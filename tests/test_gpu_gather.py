@@ -93,3 +93,22 @@ def test_gather_after_the_indexer():
     want = oracle_gather(inst, kv.numpy(), idx.numpy(), 1)
     got = _run(inst, kv, idx, 1)
     assert np.array_equal(got, want)
+
+
+def test_gather_indices_far_out_of_range():
+    """Block indices whose position index * select_block passes 2^31 (or wraps
+    to a small value in 32 bits) select nothing: their rows come out as zeros."""
+    spec, row_bytes, sel = CASES["bsnd_sel4"]
+    inst = synth.make(synth.Spec(name="far", **spec), 42)
+    rows = sum(inst["seqlens_q"])
+    g = np.random.default_rng(5)
+    idx = g.integers(-1, 20, size=(rows, inst["topk"])).astype(np.int32)
+    idx[:, 0] = 1 << 30                          # 2^30 * 4 = 2^32: wraps to 0 in int32
+    idx[:, 1] = (1 << 30) + 3                    # wraps to 12 (+ the row in the block)
+    idx[:, 2] = np.iinfo(np.int32).max
+    kv = _kv(inst, row_bytes, 43)
+    want = oracle_gather(inst, kv.numpy(), idx, sel)
+    got = _run(inst, kv, torch.from_numpy(idx), sel)
+    assert np.array_equal(got, want)
+    per = sel
+    assert not got.reshape(rows, inst["topk"] * per, row_bytes)[:, :3 * per].any()
