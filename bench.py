@@ -54,7 +54,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["li_device.h", "li_common_kernels.h", "li_pipe.h", "li_select.h",
                   "li_prefill_kernels.h", "li_prefill.hip", "li_prefill_bf16.hip",
                   "li_prefill_fp16.hip", "li_prefill_fp8.hip", "li_decode.hip", "li_metadata.hip",
-                  "li_host.cpp", "li_internal.h", "li_gather.hip"]
+                  "li_host.cpp", "li_internal.h", "li_gather.hip", "li_bucket.h", "li_grad.hip"]
 
 
 def kernel_source_hash() -> str:
