@@ -229,6 +229,11 @@ SMALL = {
                                 w_scale=0.25)),
     "list_idx_offset": (None, 52, dict(batch=1, s1=8, s2=34000, n1=8, topk=1000,
                                        idx_offset_max=1 << 20)),
+    # the boundary between workspace rows (up to 32768 keys) and candidate lists
+    "rows_32768_workspace": (None, 53, dict(batch=1, s1=6, s2=32768, n1=16, topk=2048,
+                                            w_scale=0.25)),
+    "rows_32769_lists": (None, 54, dict(batch=1, s1=6, s2=32769, n1=16, topk=2048,
+                                        w_scale=0.25)),
 }
 
 
@@ -240,8 +245,13 @@ def test_small_case(name):
     compare_all(synth.make(spec, seed))
 
 
-def test_return_value_zero_gives_same_indices():
-    inst = synth.make("tiny", 3)
+@pytest.mark.parametrize("spec", [
+    None,                                                   # rows in LDS (tiny)
+    dict(batch=1, s1=16, s2=6000, n1=16, topk=300),         # workspace rows
+    dict(batch=1, s1=8, s2=40000, n1=16, topk=700),         # candidate lists: values in the workspace
+])
+def test_return_value_zero_gives_same_indices(spec):
+    inst = synth.make("tiny", 3) if spec is None else synth.make(synth.Spec(name="rv0", **spec), 6)
     gi1, gv1 = _gpu(inst, 1)
     gi0, gv0 = _gpu(inst, 0)
     assert gv0 is None

@@ -28,7 +28,7 @@ def _dev(inst, dev):
     return g
 
 
-def _both(inst):
+def _both(inst, values=True):
     print(f"[gpu] noalloc {inst['name']} B={inst['batch']} S1={inst['max_seqlen_q']} "
           f"S2={inst['max_seqlen_k']} {inst['layout_k']}", flush=True)
     sys.stdout.flush()
@@ -45,18 +45,19 @@ def _both(inst):
         seqused_k=g["seqused_k"], cmp_residual_k=g["cmp_residual_k"],
         block_table=g["block_table"], output_idx_offset=g["output_idx_offset"])
     idx = torch.full_like(ref_i, 7)
-    val = torch.full_like(ref_v, 7.0)
+    val = torch.full_like(ref_v, 7.0) if values else None
     ptr = lambda t: None if t is None else t.data_ptr()
     st = binding.li_forward_noalloc(p, ptr(g["q"]), ptr(g["k"]), ptr(g["w"]), ptr(g["q_descale"]),
                                     ptr(g["k_descale"]), ptr(g["cu_seqlens_q"]),
                                     ptr(g["cu_seqlens_k"]), ptr(g["seqused_k"]),
                                     ptr(g["cmp_residual_k"]), ptr(g["block_table"]),
                                     ptr(g["output_idx_offset"]), meta.data_ptr(), idx.data_ptr(),
-                                    val.data_ptr(), torch.cuda.current_stream().cuda_stream)
+                                    ptr(val), torch.cuda.current_stream().cuda_stream)
     assert st == 0, binding.li_status_str(st)
     torch.cuda.synchronize()
     assert torch.equal(idx, ref_i)
-    assert torch.equal(val.view(torch.int32), ref_v.view(torch.int32))
+    if values:
+        assert torch.equal(val.view(torch.int32), ref_v.view(torch.int32))
     return p
 
 
@@ -77,3 +78,12 @@ def test_noalloc_rows_in_workspace_then_lds():
     _both(synth.make(synth.Spec(name="noalloc_global", batch=1, s1=64, s2=6000, n1=64,
                                 topk=512, w_scale=0.125), 2))
     _both(synth.make(synth.Spec(name="noalloc_lds", batch=2, s1=300, s2=300, n1=16, topk=64), 3))
+
+
+def test_noalloc_candidate_lists():
+    # rows past 32768 keys (candidate lists) without values: the running top-k's
+    # values then live in the scratch array; then a smaller list problem with values
+    _both(synth.make(synth.Spec(name="noalloc_lists", batch=1, s1=8, s2=40000, n1=16,
+                                topk=512, w_scale=0.25), 4), values=False)
+    _both(synth.make(synth.Spec(name="noalloc_lists_small", batch=1, s1=5, s2=34000, n1=8,
+                                topk=256), 5))
