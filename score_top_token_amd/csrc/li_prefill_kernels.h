@@ -15,7 +15,8 @@
 // the other is in its epilogue, select or output phase), every score in a
 // workspace row (rows up to kGlobalRowKeys keys), or a bounded candidate list
 // per row with a running threshold (longer rows).  The select is exact (ties to
-// smaller keys) and the kept keys come out in ascending key order.
+// smaller keys); the kept keys fill the output prefix in an order that depends
+// on the row mode but not on the run.
 #pragma once
 
 #include "li_common_kernels.h"

@@ -329,9 +329,9 @@ def test_paged_equals_contiguous():
     assert np.array_equal(gi, ri) and np.array_equal(gv, rv)
 
 
-# (S1, S2): decode (S1 <= 4 query rows), the dense kernel with rows in LDS, and
-# the list kernel (rows too long for LDS), with one row past 262144 keys
-@pytest.mark.parametrize("s1,s2", [(3, 300), (8, 300), (8, 12000), (8, 270000)])
+# (S1, S2): decode (S1 <= 4 query rows), the dense kernel with rows in LDS, in
+# workspace rows, and in candidate lists (rows past 32768 keys, one past 262144)
+@pytest.mark.parametrize("s1,s2", [(3, 300), (8, 300), (8, 12000), (8, 40000), (8, 270000)])
 def test_negative_infinite_scores(s1, s2):
     """Scores of -inf (from infinite inputs) still fill the top-k: ties broken by
     the smaller key, values reported as -inf, no padding while keys remain."""
