@@ -57,12 +57,18 @@ KERNEL_SOURCES = ["li_device.h", "li_common_kernels.h", "li_pipe.h", "li_select.
                   "li_host.cpp", "li_internal.h", "li_gather.hip", "li_bucket.h", "li_grad.hip"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(root: str = ROOT) -> str:
+    """Hash of the kernel sources with comments and blank space removed, so that a
+    comment edit does not count as a kernel change."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "score_top_token_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(root, "score_top_token_amd", "csrc", name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
