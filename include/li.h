@@ -141,7 +141,10 @@ li_status li_workspace_size(const li_problem* p, size_t* bytes);
  *                 j * cmp_ratio + cmp_ratio - 1 is at or before it.
  *  metadata     : device buffer of at least li_metadata_size bytes, 256-byte aligned.
  * The metadata stays valid for any li_forward call with the same problem and the
- * same length arrays; it is read-only for li_forward.
+ * same length arrays.  li_forward changes nothing in it but two words of its
+ * header, a work counter that prefill rows past 4096 keys use and leave at zero:
+ * so one metadata buffer serves one li_forward at a time (calls that may overlap
+ * on the device, on different streams, need buffers of their own).
  */
 li_status li_metadata(const li_problem* p, const int32_t* cu_seqlens_q,
                       const int32_t* cu_seqlens_k, const int32_t* seqused_k,

@@ -66,7 +66,12 @@ struct MetaHeader {
   int32_t batch;
   int32_t max_items;
   uint32_t fingerprint;   // of the li_problem the metadata was built for
-  int32_t pad[57];
+  // the persistent prefill kernels' dynamic walk of the items: the next item to
+  // take and the workgroups done; li_metadata zeroes both, and every such
+  // kernel leaves them at zero when its last workgroup ends
+  int32_t work_next;
+  int32_t work_done;
+  int32_t pad[55];
 };
 static_assert(sizeof(MetaHeader) == 256, "metadata header is 256 bytes");
 

@@ -254,6 +254,8 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
     hdr->batch = B;
     hdr->max_items = a.max_items;
     hdr->fingerprint = a.fingerprint;
+    hdr->work_next = 0;
+    hdr->work_done = 0;
   }
   __syncthreads();
 

@@ -505,11 +505,27 @@ __global__ __launch_bounds__(kDenseWaves * 64, 2) void dense_kernel(KArgs a) {
   if constexpr (RM == kRowsLds) {
     if ((int)blockIdx.x < n_items) dense_item<QK, MB, WT, KL, RM>(a, blockIdx.x, smem);
   } else {
-    for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
-      // the previous item's select scratch overlaps the K tiles (the list
-      // mode ends its items with a barrier of its own)
-      if (RM == kRowsGlobal && it != (int)blockIdx.x) __syncthreads();
+    // The fixed grid walks the work list dynamically: a workgroup takes the
+    // next item when it has finished one (a counter in the metadata header),
+    // so the slots end together whatever the items' costs (a fixed stride
+    // left the slots up to 10% apart).  The item number reaches every wave
+    // through the first LDS word, between barriers: the LDS is free between
+    // items (the select scratch and the lists are done with).
+    MetaHeader* hdr = reinterpret_cast<MetaHeader*>(a.meta);
+    int* s_item = reinterpret_cast<int*>(smem);
+    for (;;) {
+      __syncthreads();
+      if (threadIdx.x == 0) s_item[0] = atomicAdd(&hdr->work_next, 1);
+      __syncthreads();
+      const int it = s_item[0];
+      __syncthreads();                     // word 0 belongs to the item from here on
+      if (it >= n_items) break;
       dense_item<QK, MB, WT, KL, RM>(a, it, smem);
+    }
+    // the last workgroup out leaves the counters at zero for the next call
+    if (threadIdx.x == 0 && atomicAdd(&hdr->work_done, 1) == (int)gridDim.x - 1) {
+      atomicExch(&hdr->work_next, 0);
+      atomicExch(&hdr->work_done, 0);
     }
   }
 }

@@ -246,6 +246,31 @@ def test_small_case(name):
 
 
 @pytest.mark.parametrize("spec", [
+    dict(batch=2, s1=40, s2=6000, n1=16, topk=300),         # workspace rows
+    dict(batch=1, s1=12, s2=40000, n1=16, topk=512),        # candidate lists
+])
+def test_metadata_reused_across_calls(spec):
+    """The persistent prefill kernels take items through a counter in the metadata
+    header and leave it at zero: three calls on one metadata give the same bits."""
+    inst = synth.make(synth.Spec(name="meta_reuse", **spec), 7)
+    dev = torch.device("cuda")
+    g = {n: (inst[n].to(dev) if isinstance(inst.get(n), torch.Tensor) else None)
+         for n in ("q", "k", "w")}
+    p = binding.problem_for(inst, g["k"])
+    meta = binding.lightning_indexer_metadata(p, device=dev)
+    outs = [binding.lightning_indexer(p, g["q"], g["k"], g["w"], metadata=meta)
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    for i, v in outs[1:]:
+        assert torch.equal(i, outs[0][0])
+        assert torch.equal(v.view(torch.int32), outs[0][1].view(torch.int32))
+    hdr = meta[:256].view(torch.int32).cpu()
+    assert hdr[7].item() == 0 and hdr[8].item() == 0        # work_next, work_done
+    ref = binding.run_instance(inst)
+    assert torch.equal(outs[0][0], ref[0])
+
+
+@pytest.mark.parametrize("spec", [
     None,                                                   # rows in LDS (tiny)
     dict(batch=1, s1=16, s2=6000, n1=16, topk=300),         # workspace rows
     dict(batch=1, s1=8, s2=40000, n1=16, topk=700),         # candidate lists: values in the workspace
