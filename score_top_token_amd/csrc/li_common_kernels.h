@@ -63,6 +63,36 @@ __device__ inline int4 batch_rec(const KArgs& a, int b) {
   return reinterpret_cast<const int4*>(a.meta + a.off_batch)[b];
 }
 
+// The same record computed from the call's own length arguments (lightning_indexer
+// page, Constraints: inclusive cu_seqlens for TND, seqused_k for the paged keys,
+// the fixed dimensions otherwise).  The metadata kernel writes exactly this; a
+// kernel that needs only the lengths can read them without waiting for the
+// metadata.  S1_b and S2_b are held to [0, S1max] and [0, S2max], the bounds
+// every buffer is sized from (lengths past them are outside the contract).
+__device__ inline int4 batch_lengths(const KArgs& a, int b) {
+  int q_off, s1, k_off, s2;
+  if (a.layout_q == L_TND) {
+    q_off = b ? a.cu_q[b - 1] : 0;
+    s1 = a.cu_q[b] - q_off;
+  } else {
+    q_off = b * a.s1max;
+    s1 = a.s1max;
+  }
+  if (a.layout_k == L_TND) {
+    k_off = b ? a.cu_k[b - 1] : 0;
+    s2 = a.cu_k[b] - k_off;
+  } else if (a.layout_k == L_PA) {
+    k_off = 0;
+    s2 = a.seqused_k[b];
+  } else {
+    k_off = b * a.s2max;
+    s2 = a.s2max;
+  }
+  s1 = min(max(s1, 0), a.s1max);
+  s2 = min(max(s2, 0), a.s2max);
+  return int4{q_off, s1, k_off, s2};
+}
+
 // Logical key s of batch b -> (paged pool block, row).  Power-of-two block
 // sizes use shifts.
 __device__ inline void paged_slot(const KArgs& a, int b, int s, int& blk, int& r) {

@@ -501,16 +501,24 @@ __device__ __forceinline__ void select_row(SelShared& sh, const Row& row, int to
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(KArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   SelShared& sh = *reinterpret_cast<SelShared*>(smem);
-  if (!check_meta(a)) return;
+  // The grid is one workgroup per (batch, row).  Everything the row needs that
+  // does not come from the metadata (its lengths from the call's arguments, the
+  // first 64 segment ranges, the index offset) is loaded before the metadata
+  // check, so that these latencies overlap instead of queueing one after the
+  // other; the row itself follows as soon as its length is known.
   const int r = blockIdx.x;
   const int b = r / a.s1max, i = r - (r / a.s1max) * a.s1max;
-  if (b >= a.batch) return;
-  const int4 br = batch_rec(a, b);
-  if (i >= br.y) return;
   const int tid = threadIdx.x;
-  const int lim = row_limit(a, b, i, br.y, br.w);
-  const int topk = a.topk;
+  const int4 br = batch_lengths(a, b);
+  const float* mm = a.seg_mm + (int64_t)r * a.seg_mm_stride * 2;
+  const int j0 = tid & 63;
+  const bool in0 = j0 < a.seg_mm_stride;
+  const float mm_lo0 = mm[2 * (in0 ? j0 : 0)], mm_hi0 = mm[2 * (in0 ? j0 : 0) + 1];
   const int ioff = index_offset(a, b);
+  const int lim = row_limit(a, b, i, br.y, br.w);
+  if (!check_meta(a)) return;
+  if (i >= br.y) return;
+  const int topk = a.topk;
   const int64_t tok = (int64_t)br.x + i;
   int32_t* oi = a.out_idx + tok * topk;
   float* ov = a.out_val ? a.out_val + tok * topk : nullptr;
@@ -529,22 +537,27 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(KArgs a) {
     return;
   }
   // the row's range from its segments' (min, max), reduced by every wave on
-  // its own (no barrier), while the row's own loads are in flight
+  // its own (no barrier), with the row's own loads in flight
   const int chunk = reinterpret_cast<const MetaHeader*>(a.meta)->chunk;
   const int nseg = (lim + chunk - 1) / chunk;
-  const float* mm = a.seg_mm + (int64_t)r * a.seg_mm_stride * 2;
-  float mn = __builtin_inff(), mx = -__builtin_inff();
-  for (int j = tid & 63; j < nseg; j += 64) {
-    mn = fminf(mn, mm[2 * j]);
-    mx = fmaxf(mx, mm[2 * j + 1]);
-  }
-  const float lo = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_min_f(mn))));
-  const float hi = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max_f(mx))));
+  auto range = [&](float& lo, float& hi) __attribute__((always_inline)) {
+    float mn = j0 < nseg ? mm_lo0 : __builtin_inff();
+    float mx = j0 < nseg ? mm_hi0 : -__builtin_inff();
+    for (int j = j0 + 64; j < nseg; j += 64) {
+      mn = fminf(mn, mm[2 * j]);
+      mx = fmaxf(mx, mm[2 * j + 1]);
+    }
+    lo = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_min_f(mn))));
+    hi = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max_f(mx))));
+  };
+  float lo, hi;
   if (lim <= kRegRowMax) {
     RegRow row;
     row.load(src, lim);
+    range(lo, hi);
     select_row(sh, row, topk, lo, hi, oi, ov, ioff);
   } else {
+    range(lo, hi);
     const GlobalRow row{src, lim};
     select_row(sh, row, topk, lo, hi, oi, ov, ioff);
   }

@@ -25,6 +25,7 @@
 // The result depends only on the lengths (deterministic) and is produced on the
 // device, so the call never synchronises with the host.
 #include "li_pipe.h"
+#include "li_select.h"
 
 namespace li {
 
@@ -84,26 +85,10 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
   // 1. per-batch lengths (and, for decode, the visible keys of its rows)
   long long vis = 0;
   for (int b = tid; b < B; b += kMetaThreads) {
-    int q_off, s1, k_off, s2;
-    if (a.layout_q == L_TND) {
-      q_off = b ? a.cu_q[b - 1] : 0;
-      s1 = a.cu_q[b] - q_off;
-    } else {
-      q_off = b * a.s1max;
-      s1 = a.s1max;
-    }
-    if (a.layout_k == L_TND) {
-      k_off = b ? a.cu_k[b - 1] : 0;
-      s2 = a.cu_k[b] - k_off;
-    } else if (a.layout_k == L_PA) {
-      k_off = 0;
-      s2 = a.seqused_k[b];
-    } else {
-      k_off = b * a.s2max;
-      s2 = a.s2max;
-    }
-    bt[b] = int4{q_off, s1, k_off, s2};
-    if (small) s_bt[b] = int4{q_off, s1, k_off, s2};
+    const int4 rec = batch_lengths(a, b);
+    const int s1 = rec.y, s2 = rec.w;
+    bt[b] = rec;
+    if (small) s_bt[b] = rec;
     if (mode == kModeDecode)
       for (int i = 0; i < s1; ++i) vis += row_limit(a, b, i, s1, s2);
   }
@@ -112,128 +97,190 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(KArgs a, int mod
   // kDecodeSegments, more if there are many rows).  Since every row adds at
   // most one partial segment, tot / (target - rows) always fits; the candidates
   // between tot / target and that bound are counted in one pass.
-  if (mode == kModeDecode) {
-    // block sums through LDS atomics (no serial loop over the waves)
-    if (tid < kChunkCands) s_cand[tid] = 0;
-    if (tid == 0) s_tot = s_nrows = 0;
-    __syncthreads();
-    long long rows = 0;
-    for (int b = tid; b < B; b += kMetaThreads) rows += get_bt(b).y;
-    for (int o = 32; o > 0; o >>= 1) {
-      vis += __shfl_xor(vis, o);
-      rows += __shfl_xor(rows, o);
-    }
-    if (lane == 0) {
-      atomicAdd(&s_tot, (unsigned long long)vis);
-      atomicAdd(&s_nrows, (unsigned long long)rows);
-    }
-    __syncthreads();
-    const long long tot = (long long)s_tot, nrows = (long long)s_nrows;
-    long long target = kDecodeSegments;
-    while (target < 2 * nrows) target += kDecodeSegments;
-    long long c_hi = (cdiv64(tot, target - nrows) + kPipeKeys - 1) / kPipeKeys * kPipeKeys;
-    long long c_lo = (cdiv64(tot, target) + kPipeKeys - 1) / kPipeKeys * kPipeKeys;
-    if (c_lo < a.chunk) c_lo = a.chunk;
-    if (c_hi < c_lo) c_hi = c_lo;
-    // candidate c_lo + j * step, j < kChunkCands; the last one is c_hi
-    long long step = cdiv64(c_hi - c_lo, kChunkCands - 1);
-    step = (step + kPipeKeys - 1) / kPipeKeys * kPipeKeys;
-    if (step < kPipeKeys) step = kPipeKeys;
-    // thread t counts candidate t % kChunkCands over every
-    // (kMetaThreads / kChunkCands)-th batch; lanes of one candidate are then
-    // summed with three shuffles and one LDS atomic per wave.  lim and c are
-    // below 2^31: 32-bit unsigned division.
-    {
-      const int j = tid % kChunkCands;
-      const uint32_t c = (uint32_t)(j == kChunkCands - 1 ? c_hi : c_lo + j * step);
-      unsigned long long nseg = 0;
-      for (int b = tid / kChunkCands; b < B; b += kMetaThreads / kChunkCands) {
-        const int4 rec = get_bt(b);
-        for (int i = 0; i < rec.y; ++i)
-          nseg += ((uint32_t)row_limit(a, b, i, rec.y, rec.w) + c - 1u) / c;
-      }
-      for (int o = kChunkCands; o < 64; o <<= 1) nseg += __shfl_xor(nseg, o);
-      if (lane < kChunkCands && nseg) atomicAdd(&s_cand[lane], nseg);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      long long c = c_hi;
-      for (int j = kChunkCands - 1; j >= 0; --j) {
-        const long long cj = j == kChunkCands - 1 ? c_hi : c_lo + j * step;
-        if (cj <= c_hi && (long long)s_cand[j] <= target && cj < c) c = cj;
-      }
-      s_chunk = (int)c;
-    }
-  } else if (tid == 0) {
-    s_chunk = a.chunk;
-  }
-  __syncthreads();
-  const int chunk = s_chunk;
-
-  for (int b = tid; b < B; b += kMetaThreads) {
-    const int4 rec = get_bt(b);
-    int cnt = 0;
-    if (mode == kModeDecode) {
-      for (int i = 0; i < rec.y; ++i) cnt += cdiv(row_limit(a, b, i, rec.y, rec.w), chunk);
-    } else {
-      cnt = cdiv(rec.y, a.rows_per_item);
-    }
-    counts[b] = cnt;
-    if (small) s_counts[b] = cnt;
-  }
-  __syncthreads();
-
-  // 2. exclusive prefix of the counts (each thread scans a contiguous segment)
-  const int seg = cdiv(B, kMetaThreads);
-  const int b0 = tid * seg, b1 = min(b0 + seg, B);
-  int local = 0;
-  for (int b = b0; b < b1; ++b) local += get_count(b);
-  const int incl = wave_prefix_sum(local);
-  if (lane == 63) s_part[wave] = incl;
-  __syncthreads();
-  if (wave == 0) {                          // exclusive scan of the wave totals
-    const int v = lane < kMetaThreads / 64 ? s_part[lane] : 0;
-    const int inc = wave_prefix_sum(v);
-    if (lane < kMetaThreads / 64) s_part[lane] = inc - v;
-    if (lane == 63) s_total = inc;
-  }
-  __syncthreads();
-  int run = s_part[wave] + incl - local;
-  for (int b = b0; b < b1; ++b) {
-    starts[b] = run;
-    if (small) s_starts[b] = run;
-    run += get_count(b);
-  }
-  const int total = min(s_total, a.max_items);
-  // decode, small batches: segments shorter than `chunk` (at most one per row,
-  // the last) counted per batch and scanned by wave 0, four batches per lane
-  constexpr int kXcdRound = 8 * kDecodeWaves;
-  const bool xcd_deal = small && mode == kModeDecode;
-  int n_slots = total;
-  if (xcd_deal) {
+  if (SMALL && mode == kModeDecode) {
+    // Small decode batches: wave 0 alone finds the segment length and the
+    // per-batch counts, starts and short last segments (lane l holds batches
+    // 4l .. 4l+3, so the scans run in batch order), with no block barrier in
+    // between; the candidate lengths are counted with lane 8j + g taking
+    // candidate j over every 8th batch from g.
+    __syncthreads();                        // s_bt is complete
     if (wave == 0) {
-      int pc[4], sum = 0;
+      long long v = 0;
+      int nr = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int b = 4 * lane + q;
-        pc[q] = 0;
         if (b < B) {
-          const int4 rec = get_bt(b);
-          for (int i = 0; i < rec.y; ++i)
-            pc[q] += (row_limit(a, b, i, rec.y, rec.w) % chunk) != 0;
+          const int4 rec = s_bt[b];
+          nr += rec.y;
+          for (int i = 0; i < rec.y; ++i) v += row_limit(a, b, i, rec.y, rec.w);
         }
-        sum += pc[q];
       }
-      int run = wave_prefix_sum(sum) - sum;
+      for (int o = 32; o > 0; o >>= 1) {
+        v += __shfl_xor(v, o);
+        nr += __shfl_xor(nr, o);
+      }
+      const long long tot = v, nrows = nr;
+      long long target = kDecodeSegments;
+      while (target < 2 * nrows) target += kDecodeSegments;
+      long long c_hi = (cdiv64(tot, target - nrows) + kPipeKeys - 1) / kPipeKeys * kPipeKeys;
+      long long c_lo = (cdiv64(tot, target) + kPipeKeys - 1) / kPipeKeys * kPipeKeys;
+      if (c_lo < a.chunk) c_lo = a.chunk;
+      if (c_hi < c_lo) c_hi = c_lo;
+      long long step = cdiv64(c_hi - c_lo, kChunkCands - 1);
+      step = (step + kPipeKeys - 1) / kPipeKeys * kPipeKeys;
+      if (step < kPipeKeys) step = kPipeKeys;
+      static_assert(kChunkCands == 8, "eight candidates of eight lanes each");
+      const int j = lane >> 3, g = lane & 7;
+      const long long cj = j == kChunkCands - 1 ? c_hi : c_lo + j * step;
+      const uint32_t c = (uint32_t)cj;
+      unsigned long long ns = 0;
+      for (int b = g; b < B; b += 8) {
+        const int4 rec = s_bt[b];
+        for (int i = 0; i < rec.y; ++i)
+          ns += ((uint32_t)row_limit(a, b, i, rec.y, rec.w) + c - 1u) / c;
+      }
+      for (int o = 1; o < 8; o <<= 1) ns += __shfl_xor(ns, o);
+      // the shortest candidate within the budget (c_hi always is)
+      const bool ok = cj <= c_hi && (long long)ns <= target;
+      const int chunk_w = (int)min(wave_min_u(ok ? c : 0xFFFFFFFFu), (uint32_t)c_hi);
+      int cnt[4], pc[4], sc = 0, sp = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if (4 * lane + q < B) s_pstart[4 * lane + q] = run;
-        run += pc[q];
+        const int b = 4 * lane + q;
+        cnt[q] = pc[q] = 0;
+        if (b < B) {
+          const int4 rec = s_bt[b];
+          for (int i = 0; i < rec.y; ++i) {
+            const int lim = row_limit(a, b, i, rec.y, rec.w);
+            cnt[q] += cdiv(lim, chunk_w);
+            pc[q] += (lim % chunk_w) != 0;
+          }
+        }
+        sc += cnt[q];
+        sp += pc[q];
       }
-      if (lane == 63) s_npart = run;
+      int run = wave_prefix_sum(sc) - sc, prun = wave_prefix_sum(sp) - sp;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int b = 4 * lane + q;
+        if (b < B) {
+          counts[b] = cnt[q];
+          s_counts[b] = cnt[q];
+          starts[b] = run;
+          s_starts[b] = run;
+          s_pstart[b] = prun;
+        }
+        run += cnt[q];
+        prun += pc[q];
+      }
+      if (lane == 63) {
+        s_total = run;
+        s_npart = prun;
+      }
+      if (lane == 0) s_chunk = chunk_w;
     }
-    n_slots = min((total + kXcdRound - 1) / kXcdRound * kXcdRound, a.max_items);
+    __syncthreads();
+  } else {
+    if (mode == kModeDecode) {
+      // block sums through LDS atomics (no serial loop over the waves)
+      if (tid < kChunkCands) s_cand[tid] = 0;
+      if (tid == 0) s_tot = s_nrows = 0;
+      __syncthreads();
+      long long rows = 0;
+      for (int b = tid; b < B; b += kMetaThreads) rows += get_bt(b).y;
+      for (int o = 32; o > 0; o >>= 1) {
+        vis += __shfl_xor(vis, o);
+        rows += __shfl_xor(rows, o);
+      }
+      if (lane == 0) {
+        atomicAdd(&s_tot, (unsigned long long)vis);
+        atomicAdd(&s_nrows, (unsigned long long)rows);
+      }
+      __syncthreads();
+      const long long tot = (long long)s_tot, nrows = (long long)s_nrows;
+      long long target = kDecodeSegments;
+      while (target < 2 * nrows) target += kDecodeSegments;
+      long long c_hi = (cdiv64(tot, target - nrows) + kPipeKeys - 1) / kPipeKeys * kPipeKeys;
+      long long c_lo = (cdiv64(tot, target) + kPipeKeys - 1) / kPipeKeys * kPipeKeys;
+      if (c_lo < a.chunk) c_lo = a.chunk;
+      if (c_hi < c_lo) c_hi = c_lo;
+      // candidate c_lo + j * step, j < kChunkCands; the last one is c_hi
+      long long step = cdiv64(c_hi - c_lo, kChunkCands - 1);
+      step = (step + kPipeKeys - 1) / kPipeKeys * kPipeKeys;
+      if (step < kPipeKeys) step = kPipeKeys;
+      // thread t counts candidate t % kChunkCands over every
+      // (kMetaThreads / kChunkCands)-th batch; lanes of one candidate are then
+      // summed with three shuffles and one LDS atomic per wave.  lim and c are
+      // below 2^31: 32-bit unsigned division.
+      {
+        const int j = tid % kChunkCands;
+        const uint32_t c = (uint32_t)(j == kChunkCands - 1 ? c_hi : c_lo + j * step);
+        unsigned long long nseg = 0;
+        for (int b = tid / kChunkCands; b < B; b += kMetaThreads / kChunkCands) {
+          const int4 rec = get_bt(b);
+          for (int i = 0; i < rec.y; ++i)
+            nseg += ((uint32_t)row_limit(a, b, i, rec.y, rec.w) + c - 1u) / c;
+        }
+        for (int o = kChunkCands; o < 64; o <<= 1) nseg += __shfl_xor(nseg, o);
+        if (lane < kChunkCands && nseg) atomicAdd(&s_cand[lane], nseg);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        long long c = c_hi;
+        for (int j = kChunkCands - 1; j >= 0; --j) {
+          const long long cj = j == kChunkCands - 1 ? c_hi : c_lo + j * step;
+          if (cj <= c_hi && (long long)s_cand[j] <= target && cj < c) c = cj;
+        }
+        s_chunk = (int)c;
+      }
+    } else if (tid == 0) {
+      s_chunk = a.chunk;
+    }
+    __syncthreads();
+    const int chunk = s_chunk;
+
+    for (int b = tid; b < B; b += kMetaThreads) {
+      const int4 rec = get_bt(b);
+      int cnt = 0;
+      if (mode == kModeDecode) {
+        for (int i = 0; i < rec.y; ++i) cnt += cdiv(row_limit(a, b, i, rec.y, rec.w), chunk);
+      } else {
+        cnt = cdiv(rec.y, a.rows_per_item);
+      }
+      counts[b] = cnt;
+      if (small) s_counts[b] = cnt;
+    }
+    __syncthreads();
+
+    // 2. exclusive prefix of the counts (each thread scans a contiguous segment)
+    const int seg = cdiv(B, kMetaThreads);
+    const int b0 = tid * seg, b1 = min(b0 + seg, B);
+    int local = 0;
+    for (int b = b0; b < b1; ++b) local += get_count(b);
+    const int incl = wave_prefix_sum(local);
+    if (lane == 63) s_part[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {                          // exclusive scan of the wave totals
+      const int v = lane < kMetaThreads / 64 ? s_part[lane] : 0;
+      const int inc = wave_prefix_sum(v);
+      if (lane < kMetaThreads / 64) s_part[lane] = inc - v;
+      if (lane == 63) s_total = inc;
+    }
+    __syncthreads();
+    int run = s_part[wave] + incl - local;
+    for (int b = b0; b < b1; ++b) {
+      starts[b] = run;
+      if (small) s_starts[b] = run;
+      run += get_count(b);
+    }
   }
+  const int chunk = s_chunk;
+  const int total = min(s_total, a.max_items);
+  constexpr int kXcdRound = 8 * kDecodeWaves;
+  const bool xcd_deal = small && mode == kModeDecode;
+  int n_slots = total;
+  if (xcd_deal) n_slots = min((total + kXcdRound - 1) / kXcdRound * kXcdRound, a.max_items);
   if (small && (mode == kModeDenseGlobal || mode == kModeDenseList)) {
     // batches by query rows, descending (ties by index): items before batch b
     for (int b = tid; b < B; b += kMetaThreads) {
