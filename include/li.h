@@ -29,7 +29,9 @@
  *    launches nothing.
  *  - Data-dependent preconditions are not checked (undefined behaviour when
  *    violated): cu_seqlens non-decreasing with cu[B-1] equal to total_q /
- *    total_k; per-batch lengths <= max_seqlen_q / max_seqlen_k; seqused_k[b] <=
+ *    total_k; per-batch lengths <= max_seqlen_q / max_seqlen_k (the kernels
+ *    hold each length to [0, max], so a longer one is cut short rather than
+ *    read past the buffers sized from the maxima); seqused_k[b] <=
  *    max_blocks_per_seq * block_size; block_table entries in [0, num_blocks)
  *    for every block that holds a used key; descales finite and >= 0.
  *

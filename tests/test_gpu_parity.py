@@ -271,6 +271,36 @@ def test_metadata_reused_across_calls(spec):
 
 
 @pytest.mark.parametrize("spec", [
+    # decode: split kernel, select kernel (lengths from the arguments), metadata
+    dict(batch=4, s1=1, n1=16, topk=100, layout_k="PA_BSND", len_lo=500, len_hi=3000,
+         block_size=64),
+    # prefill with rows in LDS, sized from max_seqlen_k
+    dict(batch=2, s1=40, n1=16, topk=64, layout_k="PA_BSND", len_lo=300, len_hi=900,
+         block_size=32),
+])
+def test_paged_lengths_past_max_are_cut(spec):
+    """A seqused_k entry above max_seqlen_k (outside the contract) is held to
+    max_seqlen_k by every kernel: the same bits as the call with that length cut
+    to the maximum, which itself matches the oracle; nothing reads past the
+    buffers sized from the maximum (the block table has room for it: the host
+    checks max_seqlen_k <= max_blocks_per_seq * block_size)."""
+    inst = synth.make(synth.Spec(name="len_cut", **spec), 9)
+    lens = [int(x) for x in inst["seqlens_k"]]
+    cap = max(lens) - 37
+    assert sum(x > cap for x in lens) >= 1
+    longer = dict(inst)
+    longer["max_seqlen_k"] = cap                   # seqused_k keeps the longer lengths
+    cut = dict(inst)
+    cut["max_seqlen_k"] = cap
+    cut["seqlens_k"] = [min(x, cap) for x in lens]
+    cut["seqused_k"] = torch.tensor(cut["seqlens_k"], dtype=torch.int32)
+    gi_l, gv_l = _gpu(longer)
+    gi_c, gv_c, _ = compare_all(cut)
+    assert np.array_equal(gi_l, gi_c)
+    assert np.array_equal(gv_l.view(np.int32), gv_c.view(np.int32))
+
+
+@pytest.mark.parametrize("spec", [
     None,                                                   # rows in LDS (tiny)
     dict(batch=1, s1=16, s2=6000, n1=16, topk=300),         # workspace rows
     dict(batch=1, s1=8, s2=40000, n1=16, topk=700),         # candidate lists: values in the workspace
