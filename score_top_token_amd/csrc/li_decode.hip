@@ -501,7 +501,8 @@ __device__ __forceinline__ void select_row(SelShared& sh, const Row& row, int to
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(KArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   SelShared& sh = *reinterpret_cast<SelShared*>(smem);
-  // The grid is one workgroup per (batch, row).  Everything the row needs that
+  // The grid is one workgroup per (batch, row): exactly batch * S1max of them,
+  // so b < batch.  Everything the row needs that
   // does not come from the metadata (its lengths from the call's arguments, the
   // first 64 segment ranges, the index offset) is loaded before the metadata
   // check, so that these latencies overlap instead of queueing one after the
