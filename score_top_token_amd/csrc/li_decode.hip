@@ -107,7 +107,7 @@ void split_kernel(KArgs a) {
     F kb[M::KSTEPS];
     read_tile_frags<QK>(tile, lane, kb);
     mma_tile<QK, MB>(qf, kb, cur);
-    const float prev_score = block_score<MB>(prev, wv);
+    const float prev_score = block_score<MB, QK != DT_FP8>(prev, wv);
     pipe_schedule<QK, MB>();
     if (t > 0) emit(t - 1, prev_score, dprev);
     dprev = dcur;
@@ -121,7 +121,8 @@ void split_kernel(KArgs a) {
     if (t + decltype(set)::value < ntiles) step(set, t + decltype(set)::value);
   });
   const int last = ntiles - 1;
-  emit(last, (last & 1) ? block_score<MB>(accB, wv) : block_score<MB>(accA, wv), dprev);
+  constexpr bool kSwap = QK != DT_FP8;
+  emit(last, (last & 1) ? block_score<MB, kSwap>(accB, wv) : block_score<MB, kSwap>(accA, wv), dprev);
   vmin = wave_min_f(vmin);
   vmax = wave_max_f(vmax);
   if (lane == 0) {

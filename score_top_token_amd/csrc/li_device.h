@@ -163,6 +163,14 @@ __device__ inline int wave_prefix_sum(int v) {
   return v;
 }
 
+// v + (v of the lane 32 apart): the two halves of the wave exchanged by one
+// v_permlane32_swap (VALU) instead of a bpermute through the LDS.  Float addition
+// is commutative, so both lanes of a pair get the same bits.
+__device__ inline float add_half_swap(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ inline void wave_sync() { __builtin_amdgcn_wave_barrier(); __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
 
 }  // namespace li

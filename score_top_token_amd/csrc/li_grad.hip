@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kGradWaves * 64, 1) void grad_rows_kernel(GradArgs 
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             ps += __builtin_amdgcn_exp2f(fmaf(accL[mb][r], s2c, cb[mb][r]));
-        ps += __shfl_xor(ps, 32);
+        ps = add_half_swap(ps);
         if (lane < 32) {
           arrI[j0 + lane] = ok ? I : -__builtin_inff();
           arrP[j0 + lane] = ok ? ps : 0.0f;

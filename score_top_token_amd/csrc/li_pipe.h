@@ -50,8 +50,11 @@ __device__ inline void mma_tile(const typename Mma<QK>::frag (&qf)[MB][Mma<QK>::
 }
 
 // ReLU / weight / head sum of one 32-key block; lane l (and l + 32) ends with
-// the score of key l % 32.
-template <int MB>
+// the score of key l % 32.  The two half-wave sums are joined by a VALU lane
+// swap (kSwap) or by a bpermute through the LDS: the swap measures faster with
+// 16-bit keys, the LDS exchange with fp8 keys, whose epilogue is bound by VALU
+// issue.
+template <int MB, bool kSwap = true>
 __device__ inline float block_score(const f32x16 (&acc)[MB], const float (&wv)[MB][16]) {
   // one chain of fused multiply-adds: a wave64 VALU op takes four issue cycles,
   // which covers its latency, so the chain costs no more than split partial sums
@@ -61,7 +64,8 @@ __device__ inline float block_score(const f32x16 (&acc)[MB], const float (&wv)[M
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s = fmaf(wv[mb][r], relu(acc[mb][r]), s);
-  return s + __shfl_xor(s, 32);
+  if constexpr (kSwap) return add_half_swap(s);
+  else return s + __shfl_xor(s, 32);
 }
 
 // Interleave hint for one pipelined iteration: each MFMA is followed by a few

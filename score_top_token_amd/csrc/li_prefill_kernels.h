@@ -362,7 +362,7 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
     const float ds = QK == DT_FP8 ? dsc_lds[((t - 1) & (kDscSlots - 1)) * 32 + (lane & 31)] : 1.0f;
     __builtin_amdgcn_s_setprio(2);
     mma_tile<QK, MB>(qf, kb, cur);
-    const float prev_score = block_score<MB>(prev, wv);
+    const float prev_score = block_score<MB, QK != DT_FP8>(prev, wv);
     // the per-key paged addressing leaves no room for every fragment at once
     pipe_schedule<QK, MB, KL != KL_PAGED>();
     __builtin_amdgcn_s_setprio(1);
@@ -435,7 +435,8 @@ __device__ __forceinline__ void dense_item(const KArgs& a, int it, unsigned char
       }
       const int last = t - 1;              // the run covered tiles t0 .. last
       const float ds = QK == DT_FP8 ? dsc_lds[(last & (kDscSlots - 1)) * 32 + (lane & 31)] : 1.0f;
-      const float sc = (last & 1) ? block_score<MB>(accB, wv) : block_score<MB>(accA, wv);
+      constexpr bool kSwap = QK != DT_FP8;
+      const float sc = (last & 1) ? block_score<MB, kSwap>(accB, wv) : block_score<MB, kSwap>(accA, wv);
       if (last > t0) emit(last - 1, pend);
       emit(last, QK == DT_FP8 ? sc * ds : sc);
     }
