@@ -234,6 +234,14 @@ SMALL = {
                                             w_scale=0.25)),
     "rows_32769_lists": (None, 54, dict(batch=1, s1=6, s2=32769, n1=16, topk=2048,
                                         w_scale=0.25)),
+    # decode with packed (TND) queries: 0..4 query rows per sequence, so the
+    # select kernel's grid holds (batch, row) slots a sequence does not have,
+    # and key lengths from cu_seqlens_k; bf16 and fp8
+    "decode_tnd_q": (None, 55, dict(batch=7, n1=32, topk=256, layout_q="TND", layout_k="TND",
+                                    len_lo=0, len_hi=4, kv_extra=3000, w_scale=0.25)),
+    "decode_tnd_q_fp8": (None, 56, dict(batch=5, n1=64, topk=128, layout_q="TND",
+                                        layout_k="TND", len_lo=0, len_hi=3, kv_extra=900,
+                                        qk_dtype="fp8", w_scale=0.125)),
 }
 
 
