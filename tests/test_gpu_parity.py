@@ -239,6 +239,9 @@ SMALL = {
     # and key lengths from cu_seqlens_k; bf16 and fp8
     "decode_tnd_q": (None, 55, dict(batch=7, n1=32, topk=256, layout_q="TND", layout_k="TND",
                                     len_lo=0, len_hi=4, kv_extra=3000, w_scale=0.25)),
+    # 256 sequences: the largest batch whose work list one wave plans
+    "decode_b256": (None, 57, dict(batch=256, s1=2, n1=8, topk=32, layout_k="PA_BSND",
+                                   len_lo=0, len_hi=1500, block_size=32)),
     "decode_tnd_q_fp8": (None, 56, dict(batch=5, n1=64, topk=128, layout_q="TND",
                                         layout_k="TND", len_lo=0, len_hi=3, kv_extra=900,
                                         qk_dtype="fp8", w_scale=0.125)),
@@ -441,6 +444,9 @@ def _meta_items(inst):
     dict(batch=7, s1=3, n1=8, topk=64, layout_k="PA_BSND", len_lo=1, len_hi=5000, block_size=32),
     dict(batch=300, s1=2, n1=8, topk=16, layout_k="PA_BSND", len_lo=0, len_hi=3000,
          block_size=64),
+    # the largest batch the metadata kernel plans in one wave (4 batches per lane)
+    dict(batch=256, s1=4, n1=8, topk=16, layout_k="PA_BSND", len_lo=0, len_hi=2500,
+         block_size=64),
 ])
 def test_decode_work_list(spec):
     """Decode segments tile every row's visible keys exactly, start on 32-key
@@ -481,12 +487,19 @@ def test_decode_work_list(spec):
                 assert k0 == covered
                 covered = k1
             assert covered == lim, (b, i, segs[:3], lim)
-    # for these shapes the candidates are 32 apart: the segment length is the
-    # shortest multiple of 32 (>= 64, >= total / budget) that fits the budget
+    # the segment length is the shortest of eight candidates (multiples of 32
+    # from max(64, total / budget) up to total / (budget - rows), which always
+    # fits) whose segments fit the budget
     lims = [max(0, min(inst["seqlens_k"][b], i + inst["seqlens_k"][b] - spec["s1"] + 1))
             for b in range(spec["batch"]) for i in range(spec["s1"])]
-    c_lo = max(64, -(-(-(-sum(lims) // target)) // 32) * 32)
-    assert chunk == c_lo or sum(-(-x // (chunk - 32)) for x in lims) > target
+    cdiv = lambda x, y: -(-x // y)
+    tot = sum(lims)
+    c_lo = max(64, cdiv(cdiv(tot, target), 32) * 32)
+    c_hi = max(c_lo, cdiv(cdiv(tot, target - nrows), 32) * 32)
+    step = max(32, cdiv(cdiv(c_hi - c_lo, 7), 32) * 32)
+    cands = [c_lo + j * step for j in range(7)] + [c_hi]
+    fits = [c for c in cands if c <= c_hi and sum(cdiv(x, c) for x in lims) <= target]
+    assert chunk == min(fits), (chunk, cands, fits)
 
 
 @pytest.mark.parametrize("spec", [
