@@ -399,8 +399,8 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
-              "the multi-GPU sharding is a design note, not an implemented path", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU only (got --gpus {args.gpus}); "
+              "sharding across GPUs is designed, not implemented", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
